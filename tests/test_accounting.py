@@ -1,0 +1,91 @@
+"""Closed-form work/traffic counts (host logic used by the bench) pinned against the
+oracle's brute-force counts and against the figures the pages print."""
+
+import json
+import os
+
+import pytest
+
+from blockwise_ring_attention_amd import accounting as acc
+from oracle import attention as A
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.mark.parametrize("zigzag", [False, True])
+def test_allowed_entries_match_bruteforce(zigzag):
+    for c in range(1, 9):
+        for m in range(1, 8):
+            rows = 2 * m if zigzag else m
+            for rank in range(c):
+                brute = A.allowed_count(c, rank, rows, True, zigzag)
+                assert acc.allowed_entries(c, rank, rows, rows, True, zigzag) == brute
+                for t in range(c):
+                    assert acc.allowed_entries(c, rank, rows, rows, True, zigzag, t, t + 1) == \
+                        A.allowed_count(c, rank, rows, True, zigzag, t, t + 1)
+
+
+def test_zigzag_closed_form_equal_for_every_rank():
+    for c in range(1, 9):
+        for m in range(1, 8):
+            counts = {A.allowed_count(c, r, 2 * m, True, True) for r in range(c)}
+            assert counts == {(2 * c - 1) * m * m + m * (m + 1)}
+
+
+def test_load_balance_units_from_the_page():
+    g = json.load(open(os.path.join(GOLDEN, "load_balance.json")))
+    c = g["c"]
+    contiguous = [A.chunk_units(c, r, False) for r in range(c)]
+    assert contiguous == g["contiguous_units"]
+    assert max(contiguous) // min(contiguous) == g["contiguous_spread"]
+    assert all(A.chunk_units(c, r, True) == g["zigzag_units_per_rank"] for r in range(c))
+    for cc in range(1, 12):
+        assert all(A.chunk_units(cc, r, True) == 2 * cc + 1 for r in range(cc))
+        assert [A.chunk_units(cc, r, False) for r in range(cc)] == list(range(1, cc + 1))
+
+
+def test_needed_rows_match_bruteforce():
+    import numpy as np
+    for zigzag in (False, True):
+        for c in range(1, 7):
+            for m in (1, 3, 4):
+                rows = 2 * m if zigzag else m
+                for rank in range(c):
+                    pq = A.chunk_positions(rank, rows, c, zigzag)
+                    for j in range(c):
+                        pk = A.chunk_positions(j, rows, c, zigzag)
+                        brute = int(A.causal_allowed(pq, pk).any(axis=0).sum())
+                        assert acc.needed_kv_rows(c, rank, j, rows, True, zigzag) == brute
+                        assert acc.needed_kv_rows(c, rank, j, rows, False, zigzag) == rows
+    assert np.isfinite(1.0)
+
+
+def test_flop_convention_against_page():
+    g = json.load(open(os.path.join(GOLDEN, "attention_flops.json")))
+    S, L, h = g["seq"], g["layers"], g["hidden"]
+    # full rows, one layer, one head of width h: forward = 4 h S^2; fwd + bwd = 3x
+    fwd = acc.unmasked_flop(1, 1, h, acc.allowed_entries(1, 0, S, S, False, False))
+    per_token = 3 * L * fwd / S
+    assert round(per_token / 1e9) == g["gflop_per_token"]
+
+
+def test_break_even_figures_from_the_page():
+    g = json.load(open(os.path.join(GOLDEN, "ring_break_even.json")))
+    t = acc.ring_break_even_tokens(g["flops_per_s"], g["nvlink_bytes_per_s"])
+    assert round(t) == g["nvlink_tokens_per_block"]
+    assert round(6 * t, -3) == g["nvlink_tokens_per_rank_about"]
+    tp = acc.ring_break_even_tokens(g["flops_per_s"], g["port_bits_per_s"] / 8)
+    assert round(tp) == g["port_tokens_per_block"]
+    assert round(g["blocks_per_sequence"] * tp, -3) == g["port_tokens_per_rank_about"]
+
+
+def test_workload_flops_and_bytes():
+    from blockwise_ring_attention_amd.inputs import WORKLOADS
+    w = WORKLOADS["gqa64x8_d128_s128k_c16_zigzag_bf16"]
+    n = w.rows
+    e = acc.allowed_entries(w.c, w.rank, n, n, True, True)
+    assert e == 536_875_008
+    assert acc.unmasked_flop(w.batch, w.hq, w.head_dim, e) == 4 * 128 * e * 64
+    w3 = WORKLOADS["gqa32x8_d128_s32k_c8_zigzag_bf16"]
+    e3 = acc.allowed_entries(w3.c, w3.rank, w3.rows, w3.rows, True, True)
+    assert e3 == 67_110_912
