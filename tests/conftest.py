@@ -8,3 +8,16 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(scope="session")
+def ra_lib():
+    """libra.so loaded through the binding; built in-tree first if it is missing."""
+    from blockwise_ring_attention_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from blockwise_ring_attention_amd.csrc import build
+        build.build()
+    return _binding.load()

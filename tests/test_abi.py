@@ -1,0 +1,116 @@
+"""The C ABI on the CPU: the library loads, exports every entry point include/ra.h
+declares, and rejects bad arguments with the documented codes before touching the GPU
+(no call here gets as far as a launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from blockwise_ring_attention_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "ra.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(ra_lib):
+    for name in _declared_functions():
+        assert hasattr(ra_lib, name), name
+        assert ctypes.cast(getattr(ra_lib, name), ctypes.c_void_p).value
+
+
+def test_version(ra_lib):
+    assert B.version() == 100
+
+
+FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced (every call below fails its checks)
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, batch=1, hq=4, hkv=2, nq=64, nkv=64, d=128, c=4, rank=1,
+             causal=1, zigzag=1, t0=0, t1=4, dtype=B.RA_BF16)
+    a.update(kw)
+    return B.ra_rank_forward(a["q"], a["k"], a["v"], a["out"], a["lse"], a["batch"], a["hq"], a["hkv"], a["nq"],
+                             a["nkv"], a["d"], a["c"], a["rank"], a["causal"], a["zigzag"], a["t0"], a["t1"],
+                             a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), B.RA_ERR_ARG),
+    (dict(batch=-1), B.RA_ERR_ARG),
+    (dict(hq=0), B.RA_ERR_ARG),
+    (dict(hq=6, hkv=4), B.RA_ERR_ARG),
+    (dict(c=0, rank=0, t1=0), B.RA_ERR_ARG),
+    (dict(rank=4), B.RA_ERR_ARG),
+    (dict(rank=-1), B.RA_ERR_ARG),
+    (dict(t0=3, t1=2), B.RA_ERR_ARG),
+    (dict(t1=5), B.RA_ERR_ARG),
+    (dict(d=96), B.RA_ERR_UNSUPPORTED),
+    (dict(d=256), B.RA_ERR_UNSUPPORTED),
+    (dict(dtype=B.RA_F32, d=12), B.RA_ERR_UNSUPPORTED),
+    (dict(dtype=B.RA_F32, d=136), B.RA_ERR_UNSUPPORTED),
+    (dict(nkv=32), B.RA_ERR_SHAPE),
+    (dict(nq=63, nkv=63), B.RA_ERR_SHAPE),
+    (dict(c=1 << 16, rank=0, t1=1, nq=1 << 15, nkv=1 << 15), B.RA_ERR_SHAPE),
+    (dict(q=0), B.RA_ERR_ARG),
+    (dict(out=0), B.RA_ERR_ARG),
+    (dict(k=0), B.RA_ERR_ARG),
+    (dict(q=FAKE + 8), B.RA_ERR_ALIGN),
+    (dict(v=FAKE + 2), B.RA_ERR_ALIGN),
+    (dict(lse=FAKE + 2), B.RA_ERR_ALIGN),
+])
+def test_forward_argument_errors(ra_lib, kw, code):
+    assert _fwd(**kw) == code
+    assert B.last_error() != ""
+
+
+def test_forward_empty_is_a_noop(ra_lib):
+    assert _fwd(nq=0, nkv=0, q=0, k=0, v=0, out=0, lse=0, causal=0) == B.RA_OK
+    assert _fwd(batch=0, q=0, k=0, v=0, out=0, lse=0) == B.RA_OK
+
+
+def _merge(**kw):
+    a = dict(oa=FAKE, la=FAKE, ob=FAKE, lb=FAKE, o=FAKE, l=FAKE, rows=10, d=128, dtype=B.RA_BF16)
+    a.update(kw)
+    return B.ra_merge(a["oa"], a["la"], a["ob"], a["lb"], a["o"], a["l"], a["rows"], a["d"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), B.RA_ERR_ARG),
+    (dict(rows=-1), B.RA_ERR_ARG),
+    (dict(d=12), B.RA_ERR_UNSUPPORTED),
+    (dict(d=520), B.RA_ERR_UNSUPPORTED),
+    (dict(ob=0), B.RA_ERR_ARG),
+    (dict(l=0), B.RA_ERR_ARG),
+    (dict(o=FAKE + 4), B.RA_ERR_ALIGN),
+    (dict(la=FAKE + 1), B.RA_ERR_ALIGN),
+])
+def test_merge_argument_errors(ra_lib, kw, code):
+    assert _merge(**kw) == code
+
+
+def test_merge_empty_is_a_noop(ra_lib):
+    assert _merge(rows=0, oa=0, la=0, ob=0, lb=0, o=0, l=0) == B.RA_OK
+
+
+def test_check_raises_with_text(ra_lib):
+    assert _fwd(rank=9) == B.RA_ERR_ARG
+    with pytest.raises(B.RaValueError, match="rank=9"):
+        B.check(B.RA_ERR_ARG, "ra_rank_forward")
+    with pytest.raises(B.RaError):
+        B.check(B.RA_ERR_LAUNCH, "ra_rank_forward")
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        B.load(str(tmp_path / "libra.so"))

@@ -1,0 +1,179 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle, element by
+element, at sizes the oracle finishes in seconds: several query and key tiles, ragged
+tails, every mask mode, GQA groupings, round ranges, the merge, and edge cases."""
+
+import numpy as np
+import pytest
+
+import oracle
+from blockwise_ring_attention_amd.inputs import WORKLOADS, make_inputs, random_array
+from tests.gpu_util import assert_parity, run_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, hq, hkv, d, nq, nkv, c, dtype, seed, scale=1.0):
+    q = random_array((B, hq, nq, d), dtype, seed, scale)
+    k = random_array((c, B, hkv, nkv, d), dtype, seed + 1, scale)
+    v = random_array((c, B, hkv, nkv, d), dtype, seed + 2, scale)
+    return q, k, v
+
+
+CASES = [
+    # B, hq, hkv, d, n, c, rank, causal, zigzag, dtype
+    (1, 4, 1, 128, 200, 3, 1, True, True, "bf16"),      # ragged chunks (m = 100), G = 4
+    (2, 6, 2, 64, 136, 4, 2, True, False, "bf16"),      # G = 3 (one head per workgroup), d = 64
+    (1, 16, 1, 128, 96, 2, 1, True, True, "bf16"),      # G = 16: two head sets
+    (1, 8, 1, 128, 512, 4, 0, True, True, "bf16"),      # G = 8, rank 0
+    (1, 8, 2, 128, 512, 4, 3, True, True, "bf16"),      # last rank
+    (1, 2, 2, 128, 320, 5, 4, True, False, "bf16"),     # contiguous causal, last rank
+    (2, 4, 4, 128, 130, 3, 1, False, False, "bf16"),    # non-causal, ragged
+    (1, 4, 2, 128, 256, 4, 2, False, True, "bf16"),     # zigzag without mask = non-causal
+    (1, 2, 1, 64, 1000, 2, 1, True, True, "bf16"),      # odd chunk size, G = 2
+    (1, 1, 1, 64, 1024, 4, 0, True, True, "f32"),
+    (1, 2, 1, 8, 100, 3, 2, True, True, "f32"),
+    (2, 3, 1, 24, 72, 3, 0, True, False, "f32"),
+    (1, 4, 2, 40, 90, 2, 1, False, False, "f32"),
+    (1, 2, 2, 96, 128, 4, 3, True, True, "f32"),
+    (1, 4, 1, 128, 160, 2, 0, True, True, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,hq,hkv,d,n,c,rank,causal,zigzag,dtype", CASES)
+def test_fused_parity(B, hq, hkv, d, n, c, rank, causal, zigzag, dtype):
+    say(f"fused parity B={B} hq={hq} hkv={hkv} d={d} n={n} c={c} rank={rank} causal={causal} zigzag={zigzag} {dtype}")
+    q, k, v = _case(B, hq, hkv, d, n, n, c, dtype, seed=hq * 7 + n, scale=1.0)
+    out, lse = run_gpu(q, k, v, c, rank, causal, zigzag, dtype=dtype)
+    ref, ref_lse = oracle.rank_forward(q, k, v, c, rank, causal, zigzag)
+    assert_parity(out, ref, lse, ref_lse, dtype, "fused")
+
+
+def test_noncausal_nq_differs_from_nkv():
+    say("non-causal nq != nkv")
+    q, k, v = _case(2, 4, 2, 128, 70, 130, 3, "bf16", seed=5)
+    out, lse = run_gpu(q, k, v, 3, 2, False, False)
+    ref, ref_lse = oracle.rank_forward(q, k, v, 3, 2, False, False)
+    assert_parity(out, ref, lse, ref_lse, "bf16", "nq!=nkv")
+
+
+def test_tiny_worked_example_fp32():
+    w = WORKLOADS["tiny_c3_d8_fp32"]
+    say(f"workload {w.name}")
+    q, k, v = make_inputs(w)
+    out, lse = run_gpu(q, k, v, w.c, w.rank, w.causal, w.zigzag, dtype="f32")
+    ref, ref_lse = oracle.rank_forward(q, k, v, w.c, w.rank, w.causal, w.zigzag)
+    assert_parity(out, ref, lse, ref_lse, "f32", w.name)
+
+
+def test_mha_d64_s4k_zigzag_fp32_all_rows():
+    w = WORKLOADS["mha_d64_s4k_c4_zigzag_fp32"]
+    say(f"workload {w.name}")
+    q, k, v = make_inputs(w)
+    out, lse = run_gpu(q, k, v, w.c, w.rank, w.causal, w.zigzag, dtype="f32")
+    ref, ref_lse = oracle.rank_forward(q, k, v, w.c, w.rank, w.causal, w.zigzag)
+    assert_parity(out, ref, lse, ref_lse, "f32", w.name)
+
+
+@pytest.mark.parametrize("causal,zigzag,dtype", [(True, True, "bf16"), (True, False, "bf16"),
+                                                 (False, False, "bf16"), (True, True, "f32")])
+def test_round_ranges_and_masked_rows(causal, zigzag, dtype):
+    say(f"round ranges causal={causal} zigzag={zigzag} {dtype}")
+    c, n = 4, 192
+    q, k, v = _case(1, 4, 2, 128 if dtype == "bf16" else 64, n, n, c, dtype, seed=31)
+    for rank in (0, 2):
+        for t0, t1 in [(0, 1), (1, 2), (1, 3), (3, 4), (2, 2), (0, 4)]:
+            out, lse = run_gpu(q, k, v, c, rank, causal, zigzag, t0, t1, dtype=dtype)
+            ref, ref_lse = oracle.rank_forward(q, k, v, c, rank, causal, zigzag, t0, t1)
+            assert_parity(out, ref, lse, ref_lse, dtype, f"rank {rank} rounds [{t0},{t1})")
+
+
+def test_per_round_plus_merge_equals_fused():
+    import torch
+    import blockwise_ring_attention_amd as ra
+    say("per-round + merge vs fused")
+    c, n, rank = 4, 256, 1
+    q, k, v = _case(1, 8, 2, 128, n, n, c, "bf16", seed=41)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    fused, fl = ra.rank_forward(qd, kd, vd, c, rank, True, True)
+    acc, al = ra.rank_forward(qd, kd, vd, c, rank, True, True, 0, 1)
+    acc32 = acc.float()
+    for t in range(1, c):
+        part, pl = ra.rank_forward(qd, kd, vd, c, rank, True, True, t, t + 1)
+        acc32, al = ra.merge(acc32, al, part.float(), pl, out=acc32, lse=al)   # in place, fp32 carry
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.rank_forward(q, k, v, c, rank, True, True)
+    assert_parity(acc32.cpu().numpy().astype(np.float64), ref, al.cpu().numpy().astype(np.float64), ref_lse,
+                  "bf16", "merged rounds")
+    d = np.abs(acc32.cpu().numpy() - fused.float().cpu().numpy())
+    assert d.max() <= 2e-2 and d.mean() <= 2e-3
+    assert np.abs(al.cpu().numpy() - fl.cpu().numpy()).max() <= 1e-3
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 8), ("f32", 128), ("f32", 512)])
+def test_merge_parity(dtype, d):
+    import torch
+    import blockwise_ring_attention_amd as ra
+    say(f"merge parity {dtype} d={d}")
+    rows = 1000
+    rng = np.random.default_rng(d)
+    oa = random_array((rows, d), dtype, 1)
+    ob = random_array((rows, d), dtype, 2)
+    la = (rng.standard_normal(rows) * 4).astype(np.float32)
+    lb = (rng.standard_normal(rows) * 4).astype(np.float32)
+    la[::7] = -np.inf
+    lb[::11] = -np.inf
+    lb[3] = la[3] = -np.inf
+    ref_o, ref_l = oracle.merge(oa, la, ob, lb)
+    oad, obd = to_dev(oa, dtype), to_dev(ob, dtype)
+    lad, lbd = torch.from_numpy(la).cuda(), torch.from_numpy(lb).cuda()
+    o, l = ra.merge(oad, lad, obd, lbd)
+    torch.cuda.synchronize()
+    assert_parity(o.float().cpu().numpy().astype(np.float64), ref_o, l.cpu().numpy().astype(np.float64), ref_l,
+                  dtype, "merge")
+    # in place into a
+    ra.merge(oad, lad, obd, lbd, out=oad, lse=lad)
+    torch.cuda.synchronize()
+    assert np.array_equal(oad.float().cpu().numpy(), o.float().cpu().numpy())
+    assert np.array_equal(lad.cpu().numpy(), l.cpu().numpy())
+
+
+def test_no_keys_gives_zero_and_neg_inf():
+    import torch
+    import blockwise_ring_attention_amd as ra
+    say("nkv = 0 and empty round range")
+    q = to_dev(random_array((1, 2, 40, 128), "bf16", 3), "bf16")
+    k = torch.empty((2, 1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    out, lse = ra.rank_forward(q, k, k, 2, 0, False, False)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    kk = to_dev(random_array((2, 1, 2, 40, 128), "bf16", 4), "bf16")
+    out, lse = ra.rank_forward(q, kk, kk, 2, 1, True, True, 1, 1)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_lse_optional_and_repeatable():
+    import torch
+    import blockwise_ring_attention_amd as ra
+    say("lse NULL and bitwise repeatability")
+    q, k, v = _case(1, 8, 1, 128, 256, 256, 4, "bf16", seed=77)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o1, l1 = ra.rank_forward(qd, kd, vd, 4, 2, True, True)
+    o2, l2 = ra.rank_forward(qd, kd, vd, 4, 2, True, True, with_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None
+    assert torch.equal(o1, o2)
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    import blockwise_ring_attention_amd as ra
+    q = torch.zeros((1, 4, 64, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((2, 1, 3, 64, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        ra.rank_forward(q, k, k, 2, 0, True, True)          # hq % hkv != 0
+    with pytest.raises(ValueError):
+        ra.rank_forward(q, k[:, :, :2], k[:, :, :2], 2, 0, True, True)   # not contiguous
+    k2 = torch.zeros((2, 1, 2, 64, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        ra.rank_forward(torch.zeros((1, 4, 64, 96), dtype=torch.bfloat16, device="cuda"), k2, k2, 2, 0, True, True)
