@@ -143,6 +143,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (to scale the "
+                         "FETCH_SIZE/WRITE_SIZE counters against a kernel of known traffic)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one rank's share on one GPU; --gpus {args.gpus} is not supported "
@@ -150,6 +153,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
+        return
     from blockwise_ring_attention_amd import _binding
     from blockwise_ring_attention_amd.inputs import WORKLOADS
     if not os.path.exists(_binding.LIB_PATH):

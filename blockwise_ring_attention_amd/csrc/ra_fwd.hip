@@ -44,25 +44,28 @@ struct Tile {
   int row0, row_end;   // the rank's query rows [row0, row_end)
 };
 
-// Workgroup -> tile. When the (batch, KV head, head set) streams divide evenly over the
-// 8 XCDs, every tile of a stream runs on one XCD (workgroups are dealt to XCDs
-// round-robin), so the K/V tiles those workgroups share stay in that XCD's L2. Within an
-// XCD tiles go heaviest first: the last query rows see the most keys.
+// Workgroup -> tile. When the (batch, KV head) pairs divide evenly over the 8 XCDs,
+// every tile that reads one KV head runs on one XCD (workgroups are dealt to XCDs
+// round-robin), so the K/V tiles those workgroups share stay in that XCD's L2. Tiles go
+// heaviest first: the last query rows see the most keys.
 __device__ inline Tile decode_tile(const FwdArgs& a) {
   const int w = blockIdx.x;
-  int stream, qrank;
+  int bg, hset, qrank;
   if (a.xcd_map) {
-    const int xcd = w & 7, k = w >> 3, spx = a.streams >> 3;
-    stream = xcd + 8 * (k % spx);
-    qrank = k / spx;
+    const int xcd = w & 7, k = w >> 3, per = (a.B * a.hkv >> 3) * a.hsets;
+    qrank = k / per;
+    const int rem = k % per;
+    hset = rem % a.hsets;
+    bg = xcd + 8 * (rem / a.hsets);
   } else {
-    stream = w % a.streams;
+    const int stream = w % a.streams;
     qrank = w / a.streams;
+    hset = stream % a.hsets;
+    bg = stream / a.hsets;
   }
   const int qt = a.qtiles - 1 - qrank;
   Tile t;
-  t.hset = stream % a.hsets;
-  const int bg = stream / a.hsets;
+  t.hset = hset;
   t.g = bg % a.hkv;
   t.b = bg / a.hkv;
   const int half = qt / a.tiles_half;
@@ -90,7 +93,7 @@ __device__ inline int query_pos(const FwdArgs& a, int t) {
 template <int BN>
 struct KvCursor {
   int t, seg, r, rend, slim, pdelta, blk;
-  bool valid;
+  int valid;   // int, not bool: keeps the struct a plain array of words that SROA splits
 
   __device__ inline bool enter(const FwdArgs& a, int qhi) {
     blk = a.rank - t;
@@ -117,10 +120,10 @@ struct KvCursor {
   __device__ inline void seek(const FwdArgs& a, int qhi) {
     const int nseg = (a.causal && a.zigzag) ? 2 : 1;
     while (t < a.t1) {
-      if (enter(a, qhi)) { valid = true; return; }
+      if (enter(a, qhi)) { valid = 1; return; }
       if (++seg == nseg) { seg = 0; ++t; }
     }
-    valid = false;
+    valid = 0;
   }
   __device__ inline void begin(const FwdArgs& a, int qhi) {
     t = a.t0; seg = 0; seek(a, qhi);
@@ -168,40 +171,48 @@ __device__ inline float xhalf_sum(float x) {
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------- bf16 kernel
-template <int D, int BN>
+// Each workgroup is 4 waves, one 32-query column block per wave, and two workgroups
+// share a CU: the two waves on a SIMD belong to different workgroups, so while one is
+// in its softmax (VALU) the other keeps the matrix core busy, and their barriers are
+// independent.
+//
+// K/V tiles of BN = 64 keys go straight from global memory into LDS
+// (global_load_lds_dwordx4), double-buffered, so no VGPRs are spent on staging. Rows are
+// 2*D bytes, unpadded; 16-byte chunks are XOR-swizzled per row so that both the K
+// fragment reads (ds_read_b128, 16 rows per pass) and the V^T transpose reads
+// (ds_read_b64_tr_b16, 4 rows x 4 chunks per pass) hit distinct banks.
+template <int D>
 struct Bf16Layout {
-  static constexpr int KS = D * 2 + 16;   // K row stride in LDS, bytes (b128 reads conflict-free)
-  static constexpr int VS = D * 2 + 64;   // V row stride in LDS, bytes (transpose reads conflict-free)
-  static constexpr int KT = BN * KS;
-  static constexpr int VT = BN * VS;
-  static constexpr int STAGE = KT + VT;
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int CPT = BN * CPR / 256;         // chunks per thread per tensor
+  static constexpr int BN = 64;
+  static constexpr int ROWB = 2 * D;             // bytes per K or V row
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int TILE = BN * ROWB;         // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;         // K tile then V tile
+  static constexpr int RPL = 128 / D;            // rows per 256-byte bank line
+  static constexpr int LOADS = TILE / (16 * 256);  // 16-byte loads per thread per tile
+  static constexpr int NKS = D / 16;             // k-steps of QK^T
+  static constexpr int NDV = D / 32;             // 32-wide blocks of the value dimension
+  static __device__ inline int kswz(int row) { return (row / RPL) & (CPR - 1); }
+  static __device__ inline int vswz(int row) { return 4 * ((row / RPL) & (CPR / 4 - 1)); }
 };
 
-template <int D, int BN>
-struct Bf16Stage {
-  using L = Bf16Layout<D, BN>;
-  u32x4 kr[L::CPT], vr[L::CPT];
-
-  __device__ inline void load(const __bf16* kb, const __bf16* vb, int r, int nkv, int tid) {
+// Issue one stage's K and V tiles (rows r .. r+BN-1 of a block, clamped to the block)
+// into LDS. Each wave-wide load fills 1 KiB of LDS contiguously (lane i -> 16 bytes at
+// i*16), so the lane fetches the global chunk that belongs in that swizzled slot.
+template <int D>
+__device__ inline void issue_stage(char* stage, const __bf16* kb, const __bf16* vb, int r, int nkv, int wave,
+                                   int lane) {
+  using L = Bf16Layout<D>;
 #pragma unroll
-    for (int u = 0; u < L::CPT; ++u) {
-      const int q = tid + 256 * u, row = q / L::CPR, cc = q % L::CPR;
-      const size_t off = (size_t)min(r + row, nkv - 1) * D + cc * 8;
-      kr[u] = *reinterpret_cast<const u32x4*>(kb + off);
-      vr[u] = *reinterpret_cast<const u32x4*>(vb + off);
-    }
+  for (int u = 0; u < L::LOADS; ++u) {
+    const int inst = u * 4 + wave;
+    const int slot = inst * 64 + lane;
+    const int row = slot / L::CPR, phys = slot % L::CPR;
+    const size_t grow = (size_t)min(r + row, nkv - 1) * D;
+    __builtin_amdgcn_global_load_lds(kb + grow + (phys ^ L::kswz(row)) * 8, stage + inst * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + grow + (phys ^ L::vswz(row)) * 8, stage + L::TILE + inst * 1024, 16, 0, 0);
   }
-  __device__ inline void store(char* stage, int tid) {
-#pragma unroll
-    for (int u = 0; u < L::CPT; ++u) {
-      const int q = tid + 256 * u, row = q / L::CPR, cc = q % L::CPR;
-      *reinterpret_cast<u32x4*>(stage + row * L::KS + cc * 16) = kr[u];
-      *reinterpret_cast<u32x4*>(stage + L::KT + row * L::VS + cc * 16) = vr[u];
-    }
-  }
-};
+}
 
 __device__ inline bf16x8 to_bf16x8(const f32x16& s, int base) {
   bf16x8 r;
@@ -210,175 +221,176 @@ __device__ inline bf16x8 to_bf16x8(const f32x16& s, int base) {
   return r;
 }
 
+// Fold the BN keys of one stage held in LDS at `cur_buf` into the running state.
 template <int D>
-__global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int BN = 64;
-  using L = Bf16Layout<D, BN>;
-  constexpr int NKS = D / 16;   // k-steps of QK^T
-  constexpr int NDV = D / 32;   // 32-wide blocks of the value dimension
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
+__device__ __forceinline__ void fold_stage(
+    const FwdArgs& a, const KvCursor<Bf16Layout<D>::BN> cur, const char* cur_buf, int hf, int qlo, int qpos,
+    float sc, const bf16x8 (&qf)[D / 16], const int (&koff)[D / 16],
+    const int (&voff)[D / 32], f32x16 (&o)[D / 32], float& mref, float& lsum) {
+  using L = Bf16Layout<D>;
+  constexpr int BN = L::BN, NKS = L::NKS, NDV = L::NDV;
+  const char* kt = cur_buf;
+  const char* vt = cur_buf + L::TILE;
+  const bool msk = cur.needs_mask(a, qlo);
+#pragma unroll
+  for (int sub = 0; sub < BN / 32; ++sub) {
+    // S^T = K Q^T for 32 keys x 32 queries.
+    bf16x8 kf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kt + sub * 32 * L::ROWB + koff[ks]);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+    if (msk) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int krow = cur.r + sub * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+        if (!cur.key_ok(a, krow, qpos)) s[e] = kNegInf;
+      }
+    }
+    // Online softmax, one query column per lane (two halves of 16 keys each).
+    float mx = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    const float mt = xhalf_max(mx) * sc;
+    if (__builtin_amdgcn_ballot_w64(mt > mref + kTau)) {
+      const float mn = fmaxf(mref, mt);
+      // 0 when only the old reference is -inf; 1 when both are (nothing seen yet)
+      const float alpha = mn == kNegInf ? 1.f : fast_exp2(mref - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int dv = 0; dv < NDV; ++dv) o[dv] *= alpha;
+      mref = mn;
+    }
+    const float nm = mref == kNegInf ? 0.f : -mref;
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s[e] = fast_exp2(__builtin_fmaf(s[e], sc, nm));
+      ps += s[e];
+    }
+    lsum += ps;
+    // O^T += V^T P^T, 16 keys per step.
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      const bf16x8 p = to_bf16x8(s, 8 * ss);
+      const char* vb = vt + (sub * 32 + ss * 16) * L::ROWB;
+#pragma unroll
+      for (int dv = 0; dv < NDV; ++dv) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[dv]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * L::ROWB + voff[dv]));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p, o[dv], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+  using L = Bf16Layout<D>;
+  constexpr int BN = L::BN, NKS = L::NKS, NDV = L::NDV;
+  __shared__ __attribute__((aligned(1024))) char smem0[L::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[L::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, col = lane & 31;
   const Tile tile = decode_tile(a);
-
-  const __bf16* qg = static_cast<const __bf16*>(a.q);
   const __bf16* kg = static_cast<const __bf16*>(a.k);
   const __bf16* vg = static_cast<const __bf16*>(a.v);
-  __bf16* og = static_cast<__bf16*>(a.out);
 
-  // The lane's two query columns (column blocks 2*wave and 2*wave+1).
-  int head[2], row[2], qpos[2];
-  bool rvalid[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int cb = 2 * wave + nb;
-    head[nb] = tile.g * a.G + tile.hset * a.hpw + cb % a.hpw;
-    row[nb] = tile.row0 + (cb / a.hpw) * 32 + col;
-    rvalid[nb] = row[nb] < tile.row_end;
-    qpos[nb] = a.causal ? query_pos(a, min(row[nb], tile.row_end - 1)) : 0;
-  }
+  // The lane's query column: column block `wave`.
+  const int head = tile.g * a.G + tile.hset * a.hpw + wave % a.hpw;
+  const int row = tile.row0 + (wave / a.hpw) * 32 + col;
+  const bool rvalid = row < tile.row_end;
+  const int qpos = a.causal ? query_pos(a, min(row, tile.row_end - 1)) : 0;
   const int qlo = a.causal ? query_pos(a, tile.row0) : 0;
   const int qhi = a.causal ? query_pos(a, tile.row_end - 1) : 0;
 
   // Q^T fragments: lane (col, hf) holds dims 16*ks + 8*hf .. +7 of its query row.
-  bf16x8 qf[2][NKS];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const __bf16* qrow = qg + (((size_t)tile.b * a.hq + head[nb]) * a.nq + (rvalid[nb] ? row[nb] : 0)) * D;
+  bf16x8 qf[NKS];
+  {
+    const __bf16* qrow = static_cast<const __bf16*>(a.q) + (((size_t)tile.b * a.hq + head) * a.nq + (rvalid ? row : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hf);
-      if (!rvalid[nb]) x = u32x4{0, 0, 0, 0};
-      qf[nb][ks] = __builtin_bit_cast(bf16x8, x);
+      if (!rvalid) x = u32x4{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  f32x16 o[2][NDV];
+  // Swizzled LDS byte offsets of this lane's fragments within a tile.
+  int koff[NKS];   // K fragment: row sub*32 + col, chunk 2*ks + hf
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = col * L::ROWB + (((2 * ks + hf) ^ L::kswz(col)) << 4);
+  int voff[NDV];   // V^T transpose read: row 4*(g/2) + i (+ 16*ss, + 8, + 32*sub)
+  {
+    const int g = lane >> 4, i = (lane >> 2) & 3, aa = lane & 3;
+    const int vrow = 4 * (g >> 1) + i;
 #pragma unroll
-    for (int dv = 0; dv < NDV; ++dv) o[nb][dv] = f32x16{};
-  float mref[2] = {kNegInf, kNegInf};   // exponent reference, log2 units
-  float lsum[2] = {0.f, 0.f};           // this half's share of the running sum
+    for (int dv = 0; dv < NDV; ++dv) {
+      const int chunk = 4 * dv + 2 * (g & 1) + (aa >> 1);
+      voff[dv] = vrow * L::ROWB + ((chunk ^ L::vswz(vrow)) << 4) + (aa & 1) * 8;
+    }
+  }
+
+  f32x16 o[NDV];
+#pragma unroll
+  for (int dv = 0; dv < NDV; ++dv) o[dv] = f32x16{};
+  float mref = kNegInf;   // exponent reference, log2 units
+  float lsum = 0.f;       // this half's share of the running sum
   const float sc = a.scale_log2;
 
   const size_t blk_stride = (size_t)a.B * a.hkv * a.nkv * D;
   const size_t head_off = ((size_t)tile.b * a.hkv + tile.g) * a.nkv * D;
 
-  // Transpose-read addressing of V^T fragments (see the kernel header).
-  const int g16 = lane >> 4, i4 = (lane >> 2) & 3, a4 = lane & 3;
-  const int v_lane_off = (4 * (g16 >> 1) + i4) * L::VS + (16 * (g16 & 1) + 4 * a4) * 2;
-
-  KvCursor<BN> cur;
-  cur.begin(a, qhi);
-  Bf16Stage<D, BN> st;
-  int buf = 0;
-  if (cur.valid) {
-    st.load(kg + cur.blk * blk_stride + head_off, vg + cur.blk * blk_stride + head_off, cur.r, a.nkv, tid);
-    st.store(smem, tid);
-  }
-  __syncthreads();
-
-  while (cur.valid) {
-    KvCursor<BN> nxt = cur;
-    nxt.next(a, qhi);
-    if (nxt.valid)
-      st.load(kg + nxt.blk * blk_stride + head_off, vg + nxt.blk * blk_stride + head_off, nxt.r, a.nkv, tid);
-
-    const char* kl = smem + buf * L::STAGE;
-    const char* vl = kl + L::KT;
-    const bool msk = cur.needs_mask(a, qlo);
-
-#pragma unroll
-    for (int sub = 0; sub < BN / 32; ++sub) {
-      // S^T = K Q^T for 32 keys x (2 x 32) queries.
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + (sub * 32 + col) * L::KS + (16 * ks + 8 * hf) * 2);
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][ks], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[1][ks], s[1], 0, 0, 0);
-      }
-      if (msk) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int krow = cur.r + sub * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-            if (!cur.key_ok(a, krow, qpos[nb])) s[nb][e] = kNegInf;
-          }
-      }
-      // Online softmax, one query column per lane.
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float mx = s[nb][0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[nb][e]);
-        const float mt = xhalf_max(mx) * sc;
-        if (__builtin_amdgcn_ballot_w64(mt > mref[nb] + kTau)) {
-          const float mn = fmaxf(mref[nb], mt);
-          // 0 when only the old reference is -inf; 1 when both are (nothing seen yet)
-          const float alpha = mn == kNegInf ? 1.f : fast_exp2(mref[nb] - mn);
-          lsum[nb] *= alpha;
-#pragma unroll
-          for (int dv = 0; dv < NDV; ++dv) o[nb][dv] *= alpha;
-          mref[nb] = mn;
-        }
-        const float nm = mref[nb] == kNegInf ? 0.f : -mref[nb];
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(s[nb][e], sc, nm));
-          s[nb][e] = p;
-          ps += p;
-        }
-        lsum[nb] += ps;
-      }
-      // O^T += V^T P^T, 16 keys per step.
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        const bf16x8 p0 = to_bf16x8(s[0], 8 * ss);
-        const bf16x8 p1 = to_bf16x8(s[1], 8 * ss);
-        const char* vb = vl + (sub * 32 + 16 * ss) * L::VS + v_lane_off;
-#pragma unroll
-        for (int dv = 0; dv < NDV; ++dv) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + dv * 64));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * L::VS + dv * 64));
-          const s16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 va = __builtin_bit_cast(bf16x8, v8);
-          o[0][dv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p0, o[0][dv], 0, 0, 0);
-          o[1][dv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1, o[1][dv], 0, 0, 0);
-        }
-      }
-    }
-
-    if (nxt.valid) st.store(smem + (buf ^ 1) * L::STAGE, tid);
+  // Stages alternate between two LDS buffers. They are distinct arrays and the loop is
+  // unrolled over them, so the compiler can tell one stage's reads apart from the
+  // in-flight loads of the next (one shared array would make it wait for those loads
+  // before every LDS read). At each step: wait for this stage's own loads and the
+  // barrier (all waves' loads visible; the other buffer's old stage read by everyone),
+  // start streaming the next stage, then fold this one.
+  KvCursor<BN> c0, c1;
+  c0.begin(a, qhi);
+  if (c0.valid)
+    issue_stage<D>(smem0, kg + c0.blk * blk_stride + head_off, vg + c0.blk * blk_stride + head_off, c0.r, a.nkv,
+                   wave, lane);
+  while (c0.valid) {
+    c1 = c0;
+    c1.next(a, qhi);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    cur = nxt;
-    buf ^= 1;
+    if (c1.valid)
+      issue_stage<D>(smem1, kg + c1.blk * blk_stride + head_off, vg + c1.blk * blk_stride + head_off, c1.r, a.nkv,
+                     wave, lane);
+    fold_stage<D>(a, c0, smem0, hf, qlo, qpos, sc, qf, koff, voff, o, mref, lsum);
+    if (!c1.valid) break;
+    c0 = c1;
+    c0.next(a, qhi);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c0.valid)
+      issue_stage<D>(smem0, kg + c0.blk * blk_stride + head_off, vg + c0.blk * blk_stride + head_off, c0.r, a.nkv,
+                     wave, lane);
+    fold_stage<D>(a, c1, smem1, hf, qlo, qpos, sc, qf, koff, voff, o, mref, lsum);
   }
 
   // Epilogue: out = O / sum, lse = ln(sum) + reference.
+  const float lt = xhalf_sum(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (!rvalid) return;
+  const size_t ridx = ((size_t)tile.b * a.hq + head) * a.nq + row;
+  __bf16* orow = static_cast<__bf16*>(a.out) + ridx * D;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float lt = xhalf_sum(lsum[nb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (!rvalid[nb]) continue;
-    const size_t ridx = ((size_t)tile.b * a.hq + head[nb]) * a.nq + row[nb];
-    __bf16* orow = og + ridx * D;
+  for (int dv = 0; dv < NDV; ++dv)
 #pragma unroll
-    for (int dv = 0; dv < NDV; ++dv)
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = (__bf16)(o[nb][dv][4 * i + j] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf) = w;
-      }
-    if (a.lse != nullptr && hf == 0)
-      a.lse[ridx] = lt > 0.f ? (mref[nb] + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
-  }
+      for (int j = 0; j < 4; ++j) w[j] = (__bf16)(o[dv][4 * i + j] * inv);
+      *reinterpret_cast<bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf) = w;
+    }
+  if (a.lse != nullptr && hf == 0) a.lse[ridx] = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------- fp32 kernel

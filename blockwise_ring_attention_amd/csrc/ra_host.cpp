@@ -92,7 +92,7 @@ extern "C" int ra_rank_forward(const void* q, const void* k_blocks, const void* 
   const long long grid = streams * a.qtiles;
   if (grid > INT_MAX) return fail(RA_ERR_SHAPE, "too many tiles (%lld)", grid);
   a.streams = (int)streams;
-  a.xcd_map = (streams % 8) == 0;
+  a.xcd_map = ((long long)batch * hkv) % 8 == 0;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
 
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -24,17 +24,16 @@ struct FwdArgs {
   int tiles_half;       // ceil(rows_half / prow)
   int qtiles;           // nhalves * tiles_half
   int streams;          // B * hkv * hsets: independent (batch, KV head, head set) units
-  int xcd_map;          // 1: streams % 8 == 0, pin each stream to one XCD
+  int xcd_map;          // 1: (B * hkv) % 8 == 0, pin each KV head to one XCD
   float scale_log2;     // log2(e) / sqrt(d)
 };
 
 // Column blocks (of 32 query rows each) per workgroup, per kernel family.
-constexpr int kBf16ColBlocks = 8;   // 4 waves x 2 column blocks
+constexpr int kBf16ColBlocks = 4;   // 4 waves x 1 column block
 constexpr int kF32ColBlocks = 4;    // 4 waves x 1 column block
 
 hipError_t launch_forward_bf16(const FwdArgs& a, int grid, hipStream_t stream);
 hipError_t launch_forward_f32(const FwdArgs& a, int grid, hipStream_t stream);
-hipError_t launch_fill_empty(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_merge(const void* oa, const float* la, const void* ob, const float* lb, void* out,
                         float* lse, long long rows, int d, int dtype, hipStream_t stream);
 
