@@ -30,10 +30,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
-// The running maximum used as the exponent reference is only raised when a tile's
-// maximum exceeds it by more than 2^kTau (log2 units). Exponentials then stay below
-// 2^kTau; numerator and denominator share the reference, so the result is unchanged.
+// The exponent reference is a running maximum raised lazily. Exponentials are taken
+// against the current reference; it is raised (to the true running maximum, with O and
+// the row sum rescaled) only when the reference is unset or some exponential may exceed
+// 2^kTau, so exponentials stay below 2^kTau. Numerator and denominator share the
+// reference, so the result is unchanged.
 constexpr float kTau = 8.0f;
+constexpr float kBig = 256.0f;   // 2^kTau
 constexpr float kLn2 = 0.693147180559945309f;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -196,23 +199,50 @@ struct Bf16Layout {
   static __device__ inline int vswz(int row) { return 4 * ((row / RPL) & (CPR / 4 - 1)); }
 };
 
-// Issue one stage's K and V tiles (rows r .. r+BN-1 of a block, clamped to the block)
-// into LDS. Each wave-wide load fills 1 KiB of LDS contiguously (lane i -> 16 bytes at
-// i*16), so the lane fetches the global chunk that belongs in that swizzled slot.
+// Issue one stage's K and V tiles (rows r .. r+BN-1 of a block) into LDS. Each wave-wide
+// load fills 1 KiB of LDS contiguously (lane i -> 16 bytes at i*16), so the lane fetches
+// the global chunk that belongs in that swizzled slot: `koff`/`voff` hold those per-lane
+// byte offsets relative to row r, and the per-stage base is uniform. A stage that runs
+// past the block's last row (only the last, ragged tile of a block) clamps rows instead.
 template <int D>
-__device__ inline void issue_stage(char* stage, const __bf16* kb, const __bf16* vb, int r, int nkv, int wave,
-                                   int lane) {
+struct StageLoader {
   using L = Bf16Layout<D>;
+  unsigned koff[L::LOADS], voff[L::LOADS];   // unsigned: lets the loads use a scalar base
+  int row[L::LOADS];
+  int wave;   // wave-uniform
+
+  __device__ inline void init(int wave_uniform, int lane) {
+    wave = wave_uniform;
 #pragma unroll
-  for (int u = 0; u < L::LOADS; ++u) {
-    const int inst = u * 4 + wave;
-    const int slot = inst * 64 + lane;
-    const int row = slot / L::CPR, phys = slot % L::CPR;
-    const size_t grow = (size_t)min(r + row, nkv - 1) * D;
-    __builtin_amdgcn_global_load_lds(kb + grow + (phys ^ L::kswz(row)) * 8, stage + inst * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vb + grow + (phys ^ L::vswz(row)) * 8, stage + L::TILE + inst * 1024, 16, 0, 0);
+    for (int u = 0; u < L::LOADS; ++u) {
+      const int slot = (u * 4 + wave) * 64 + lane;
+      row[u] = slot / L::CPR;
+      const int phys = slot % L::CPR;
+      koff[u] = row[u] * L::ROWB + ((phys ^ L::kswz(row[u])) << 4);
+      voff[u] = row[u] * L::ROWB + ((phys ^ L::vswz(row[u])) << 4);
+    }
   }
-}
+
+  __device__ inline void issue(char* stage, const __bf16* kb, const __bf16* vb, int r, int nkv) const {
+    const char* kr = reinterpret_cast<const char*>(kb + (size_t)r * D);
+    const char* vr = reinterpret_cast<const char*>(vb + (size_t)r * D);
+    if (r + L::BN <= nkv) {
+#pragma unroll
+      for (int u = 0; u < L::LOADS; ++u) {
+        __builtin_amdgcn_global_load_lds(kr + koff[u], stage + (u * 4 + wave) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vr + voff[u], stage + L::TILE + (u * 4 + wave) * 1024, 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < L::LOADS; ++u) {
+        // rows past the block repeat its last row (masked out by the fold)
+        const unsigned back = max(0, r + row[u] - (nkv - 1)) * L::ROWB;
+        __builtin_amdgcn_global_load_lds(kr + koff[u] - back, stage + (u * 4 + wave) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vr + voff[u] - back, stage + L::TILE + (u * 4 + wave) * 1024, 16, 0, 0);
+      }
+    }
+  }
+};
 
 __device__ inline bf16x8 to_bf16x8(const f32x16& s, int base) {
   bf16x8 r;
@@ -249,31 +279,45 @@ __device__ __forceinline__ void fold_stage(
       }
     }
     // Online softmax, one query column per lane (two halves of 16 keys each).
-    float mx = s[0];
+    // Fast path: exponentials against the current reference. Every p is positive, so a
+    // half-row whose sum stays within 2^kTau has every p within 2^kTau and needs no new
+    // reference. Otherwise -- a reference not yet set (-inf), or a score that passed it
+    // by more than kTau -- the wave takes the row maximum, raises the reference,
+    // rescales O and the sum, and recomputes p.
+    f32x16 p32;
+    float ps = 0.f;
+    {
+      const float nm = mref == kNegInf ? 0.f : -mref;
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-    const float mt = xhalf_max(mx) * sc;
-    if (__builtin_amdgcn_ballot_w64(mt > mref + kTau)) {
-      const float mn = fmaxf(mref, mt);
+      for (int e = 0; e < 16; ++e) {
+        p32[e] = fast_exp2(__builtin_fmaf(s[e], sc, nm));
+        ps += p32[e];
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(mref == kNegInf || ps > kBig)) {
+      float mx = s[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      const float mn = fmaxf(mref, xhalf_max(mx) * sc);
       // 0 when only the old reference is -inf; 1 when both are (nothing seen yet)
       const float alpha = mn == kNegInf ? 1.f : fast_exp2(mref - mn);
       lsum *= alpha;
 #pragma unroll
       for (int dv = 0; dv < NDV; ++dv) o[dv] *= alpha;
       mref = mn;
-    }
-    const float nm = mref == kNegInf ? 0.f : -mref;
-    float ps = 0.f;
+      const float nm = mref == kNegInf ? 0.f : -mref;
+      ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      s[e] = fast_exp2(__builtin_fmaf(s[e], sc, nm));
-      ps += s[e];
+      for (int e = 0; e < 16; ++e) {
+        p32[e] = fast_exp2(__builtin_fmaf(s[e], sc, nm));
+        ps += p32[e];
+      }
     }
     lsum += ps;
     // O^T += V^T P^T, 16 keys per step.
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss) {
-      const bf16x8 p = to_bf16x8(s, 8 * ss);
+      const bf16x8 p = to_bf16x8(p32, 8 * ss);
       const char* vb = vt + (sub * 32 + ss * 16) * L::ROWB;
 #pragma unroll
       for (int dv = 0; dv < NDV; ++dv) {
@@ -293,11 +337,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem0[L::STAGE];
   __shared__ __attribute__((aligned(1024))) char smem1[L::STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, col = lane & 31;
   const Tile tile = decode_tile(a);
   const __bf16* kg = static_cast<const __bf16*>(a.k);
   const __bf16* vg = static_cast<const __bf16*>(a.v);
+  StageLoader<D> ld;
+  ld.init(wave, lane);
 
   // The lane's query column: column block `wave`.
   const int head = tile.g * a.G + tile.hset * a.hpw + wave % a.hpw;
@@ -353,16 +400,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   KvCursor<BN> c0, c1;
   c0.begin(a, qhi);
   if (c0.valid)
-    issue_stage<D>(smem0, kg + c0.blk * blk_stride + head_off, vg + c0.blk * blk_stride + head_off, c0.r, a.nkv,
-                   wave, lane);
+    ld.issue(smem0, kg + c0.blk * blk_stride + head_off, vg + c0.blk * blk_stride + head_off, c0.r, a.nkv);
   while (c0.valid) {
     c1 = c0;
     c1.next(a, qhi);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (c1.valid)
-      issue_stage<D>(smem1, kg + c1.blk * blk_stride + head_off, vg + c1.blk * blk_stride + head_off, c1.r, a.nkv,
-                     wave, lane);
+      ld.issue(smem1, kg + c1.blk * blk_stride + head_off, vg + c1.blk * blk_stride + head_off, c1.r, a.nkv);
     fold_stage<D>(a, c0, smem0, hf, qlo, qpos, sc, qf, koff, voff, o, mref, lsum);
     if (!c1.valid) break;
     c0 = c1;
@@ -370,8 +415,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (c0.valid)
-      issue_stage<D>(smem0, kg + c0.blk * blk_stride + head_off, vg + c0.blk * blk_stride + head_off, c0.r, a.nkv,
-                     wave, lane);
+      ld.issue(smem0, kg + c0.blk * blk_stride + head_off, vg + c0.blk * blk_stride + head_off, c0.r, a.nkv);
     fold_stage<D>(a, c1, smem1, hf, qlo, qpos, sc, qf, koff, voff, o, mref, lsum);
   }
 

@@ -21,7 +21,8 @@
  *     enqueued on it and the call returns without waiting.
  *   - Every argument is checked on the host before anything is enqueued. A nonzero
  *     return means nothing was enqueued and no output was touched; ra_last_error()
- *     then describes the problem. Non-finite inputs are not checked and propagate.
+ *     then describes the problem. Inputs are not checked for NaN or infinity; results
+ *     for non-finite inputs are unspecified.
  *   - Calls are reentrant; the last-error text is per host thread.
  */
 #ifndef RA_H
