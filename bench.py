@@ -91,23 +91,31 @@ def time_workload(w, steps: int, warmup: int, arrays=None):
     return wall / steps * 1e3, sum(launch_ms) / len(launch_ms), min(launch_ms)
 
 
-def cpu_baseline(w, arrays, budget_rows: int = 96):
-    """The oracle as it stands, on a bounded sample of the same workload: full rows of
-    query rows spread over the share, for one (batch, head), in fp64 on the host."""
+def cpu_baseline(w, arrays, min_seconds: float = 10.0):
+    """The oracle as it stands, timed on a bounded sample of the same workload: the first
+    R query rows of batch 0 in head-major order, each as a full fp64 row against every
+    key of the c blocks. R starts at 96 and doubles until one run of the oracle takes
+    at least `min_seconds` (or covers the whole share); that run is reported."""
     import numpy as np
     import oracle
     q, k, v = arrays
     n = w.rows
-    rng = np.random.default_rng(1234)
-    ts = np.sort(rng.choice(n, size=min(budget_rows, n), replace=False))
-    rows = np.stack([np.zeros_like(ts), np.zeros_like(ts), ts], axis=1)
-    t0 = time.perf_counter()
-    oracle.rank_forward(q, k, v, w.c, w.rank, w.causal, w.zigzag, rows=rows)
-    sec = time.perf_counter() - t0
+    total_rows = w.hq * n
+    count = 96
+    while True:
+        count = min(count, total_rows)
+        idx = np.arange(count)
+        rows = np.stack([np.zeros_like(idx), idx // n, idx % n], axis=1)
+        t0 = time.perf_counter()
+        oracle.rank_forward(q, k, v, w.c, w.rank, w.causal, w.zigzag, rows=rows)
+        sec = time.perf_counter() - t0
+        if sec >= min_seconds or count == total_rows:
+            break
+        count *= 2
     # unmasked work of the sampled rows: allowed keys per row
+    ts = rows[:, 2]
     if w.causal:
-        pq = oracle.chunk_positions(w.rank, n, w.c, w.zigzag)[ts]
-        allowed = int((pq + 1).sum())
+        allowed = int((oracle.chunk_positions(w.rank, n, w.c, w.zigzag)[ts] + 1).sum())
     else:
         allowed = len(ts) * n * w.c
     flop = 4 * w.head_dim * allowed
@@ -127,9 +135,9 @@ def cpu_baseline(w, arrays, budget_rows: int = 96):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"{len(ts)} random query rows of batch 0, head 0 of {w.name}, each against every key of the "
-                   f"{w.c} blocks (full-row fp64 brute force, masked entries computed and discarded); "
-                   f"{sec:.1f} s wall; rate counts unmasked work only"),
+        "sample": (f"first {count} query rows (head-major, batch 0) of {w.name}, each a full fp64 row "
+                   f"against all {w.c * n} keys (masked entries computed and discarded); {sec:.1f} s wall; "
+                   f"rate counts unmasked work only"),
         "seconds": sec,
     }
 
@@ -142,7 +150,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum length of the timed oracle run for cpu_baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (to scale the "
                          "FETCH_SIZE/WRITE_SIZE counters against a kernel of known traffic)")
@@ -209,7 +218,7 @@ def main():
                          "pct_of_peak": round(100 * fa / (ms_a * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)})
         line["also"] = also
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, arrays, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(w, arrays, args.cpu_seconds)
     torch.cuda.synchronize()
     print(json.dumps(line), flush=True)
 
