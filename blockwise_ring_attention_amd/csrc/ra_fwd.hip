@@ -38,6 +38,9 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kTau = 8.0f;
 constexpr float kBig = 256.0f;   // 2^kTau
 constexpr float kLn2 = 0.693147180559945309f;
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle; accesses at or past num_records bytes are out of range.
+constexpr int kBufferFlags = 0x00020000;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -174,40 +177,49 @@ __device__ inline float xhalf_sum(float x) {
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------- bf16 kernel
-// Each workgroup is 4 waves, one 32-query column block per wave, and two workgroups
-// share a CU: the two waves on a SIMD belong to different workgroups, so while one is
-// in its softmax (VALU) the other keeps the matrix core busy, and their barriers are
-// independent.
+// A workgroup is 8 waves, one 32-query column block each, and fills a CU (two waves per
+// SIMD): every K/V stage staged in LDS serves 256 query columns.
 //
-// K/V tiles of BN = 64 keys go straight from global memory into LDS
-// (global_load_lds_dwordx4), double-buffered, so no VGPRs are spent on staging. Rows are
-// 2*D bytes, unpadded; 16-byte chunks are XOR-swizzled per row so that both the K
-// fragment reads (ds_read_b128, 16 rows per pass) and the V^T transpose reads
-// (ds_read_b64_tr_b16, 4 rows x 4 chunks per pass) hit distinct banks.
+// K/V stages of BN = 64 keys go straight from global memory into LDS (buffer loads that
+// write LDS), so no VGPRs are spent on staging; NB stage buffers keep up to NB - 3 stages
+// in flight behind the one being folded. Rows are 2*D bytes, unpadded; 16-byte chunks are
+// XOR-swizzled per row so that both the K fragment reads (ds_read_b128, 16 rows per pass)
+// and the V^T transpose reads (ds_read_b64_tr_b16, 4 rows x 4 chunks per pass) hit
+// distinct banks.
+//
+// Each wave folds its keys as a software pipeline over 32-key sub-tiles: step t issues
+// the MFMAs of S = K Q^T for sub-tile t+1 and of O^T += V^T P^T for sub-tile t-1, and in
+// the same basic block the vector ALU computes the softmax of sub-tile t, so the matrix
+// core is fed from the wave's own instruction stream while its exponentials run.
 template <int D>
 struct Bf16Layout {
-  static constexpr int BN = 64;
+  static constexpr int BN = 64;                  // keys per stage
+  static constexpr int WAVES = 8;
   static constexpr int ROWB = 2 * D;             // bytes per K or V row
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int TILE = BN * ROWB;         // bytes of one K (or V) tile
   static constexpr int STAGE = 2 * TILE;         // K tile then V tile
+  static constexpr int NB = 5;                   // stage buffers (5 x 32 KiB = all LDS at D = 128)
   static constexpr int RPL = 128 / D;            // rows per 256-byte bank line
-  static constexpr int LOADS = TILE / (16 * 256);  // 16-byte loads per thread per tile
-  static constexpr int NKS = D / 16;             // k-steps of QK^T
+  static constexpr int LOADS = TILE / (16 * 64 * WAVES);  // 16-byte loads per thread per tile
+  static constexpr int NKS = D / 16;             // k-steps of QK^T per 32-key sub-tile
   static constexpr int NDV = D / 32;             // 32-wide blocks of the value dimension
   static __device__ inline int kswz(int row) { return (row / RPL) & (CPR - 1); }
   static __device__ inline int vswz(int row) { return 4 * ((row / RPL) & (CPR / 4 - 1)); }
 };
 
-// Issue one stage's K and V tiles (rows r .. r+BN-1 of a block) into LDS. Each wave-wide
-// load fills 1 KiB of LDS contiguously (lane i -> 16 bytes at i*16), so the lane fetches
-// the global chunk that belongs in that swizzled slot: `koff`/`voff` hold those per-lane
-// byte offsets relative to row r, and the per-stage base is uniform. A stage that runs
-// past the block's last row (only the last, ragged tile of a block) clamps rows instead.
+// Issue one stage's K and V tiles (rows r .. r+BN-1 of one (block, batch, KV head) slab)
+// into LDS with buffer loads that write LDS directly (buffer_load_dwordx4 ... lds). Each
+// wave-wide load fills 1 KiB of LDS contiguously (lane i -> 16 bytes at i*16), so the
+// lane fetches the global chunk that belongs in that swizzled slot: `koff`/`voff` hold
+// those per-lane byte offsets relative to row r, and the row offset is a scalar. A stage
+// that runs past the slab's last row (only the last, ragged tile of a block) clamps rows
+// instead, so every load stays inside the slab. (The buffer form, unlike the global
+// one, lets the compiler count LDS reads precisely while these loads are in flight.)
 template <int D>
 struct StageLoader {
   using L = Bf16Layout<D>;
-  unsigned koff[L::LOADS], voff[L::LOADS];   // unsigned: lets the loads use a scalar base
+  unsigned koff[L::LOADS], voff[L::LOADS];
   int row[L::LOADS];
   int wave;   // wave-uniform
 
@@ -215,7 +227,7 @@ struct StageLoader {
     wave = wave_uniform;
 #pragma unroll
     for (int u = 0; u < L::LOADS; ++u) {
-      const int slot = (u * 4 + wave) * 64 + lane;
+      const int slot = (u * L::WAVES + wave) * 64 + lane;
       row[u] = slot / L::CPR;
       const int phys = slot % L::CPR;
       koff[u] = row[u] * L::ROWB + ((phys ^ L::kswz(row[u])) << 4);
@@ -223,26 +235,62 @@ struct StageLoader {
     }
   }
 
+  // kb, vb: row 0 of the slab (nkv rows of 2*D bytes; nkv * 2 * D < 2^31 is checked on
+  // the host).
   __device__ inline void issue(char* stage, const __bf16* kb, const __bf16* vb, int r, int nkv) const {
-    const char* kr = reinterpret_cast<const char*>(kb + (size_t)r * D);
-    const char* vr = reinterpret_cast<const char*>(vb + (size_t)r * D);
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int bytes = nkv * L::ROWB;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, bytes, kBufferFlags);
+    const int soff = r * L::ROWB;
     if (r + L::BN <= nkv) {
 #pragma unroll
       for (int u = 0; u < L::LOADS; ++u) {
-        __builtin_amdgcn_global_load_lds(kr + koff[u], stage + (u * 4 + wave) * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vr + voff[u], stage + L::TILE + (u * 4 + wave) * 1024, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(stage + (u * L::WAVES + wave) * 1024), 16, koff[u],
+                                                 soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(stage + L::TILE + (u * L::WAVES + wave) * 1024), 16,
+                                                 voff[u], soff, 0, 0);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < L::LOADS; ++u) {
-        // rows past the block repeat its last row (masked out by the fold)
-        const unsigned back = max(0, r + row[u] - (nkv - 1)) * L::ROWB;
-        __builtin_amdgcn_global_load_lds(kr + koff[u] - back, stage + (u * 4 + wave) * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vr + voff[u] - back, stage + L::TILE + (u * 4 + wave) * 1024, 16, 0, 0);
+        // rows past the slab repeat its last row (masked out by the fold)
+        const int back = max(0, r + row[u] - (nkv - 1)) * L::ROWB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(stage + (u * L::WAVES + wave) * 1024), 16,
+                                                 soff + (int)koff[u] - back, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(stage + L::TILE + (u * L::WAVES + wave) * 1024), 16,
+                                                 soff + (int)voff[u] - back, 0, 0, 0);
       }
     }
   }
 };
+
+// Wait until at most `stages` stages of this thread's K/V loads are still in flight
+// (loads complete in issue order). The counts are immediates, hence the branches.
+template <int D>
+__device__ __forceinline__ void wait_stages(int stages) {
+  constexpr int N = 2 * Bf16Layout<D>::LOADS;   // loads per stage per thread
+  static_assert(3 * N < 64, "vmcnt field");
+  if (stages >= 3)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((3 * N) & 15) | (((3 * N) >> 4) << 14));
+  else if (stages == 2)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * N) & 15) | (((2 * N) >> 4) << 14));
+  else if (stages == 1)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Workgroup barrier between phases. No instruction is scheduled across it, and the
+// memory clobber keeps the compiler from moving loads or stores over it. It waits for no
+// memory counter: every LDS read of a phase feeds an MFMA of the same phase, so it has
+// returned before the wave arrives, and K/V loads are waited for explicitly
+// (wait_stages), which a workgroup fence would instead drain completely.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 __device__ inline bf16x8 to_bf16x8(const f32x16& s, int base) {
   bf16x8 r;
@@ -251,53 +299,115 @@ __device__ inline bf16x8 to_bf16x8(const f32x16& s, int base) {
   return r;
 }
 
-// Fold the BN keys of one stage held in LDS at `cur_buf` into the running state.
-template <int D>
-__device__ __forceinline__ void fold_stage(
-    const FwdArgs& a, const KvCursor<Bf16Layout<D>::BN> cur, const char* cur_buf, int hf, int qlo, int qpos,
-    float sc, const bf16x8 (&qf)[D / 16], const int (&koff)[D / 16],
-    const int (&voff)[D / 32], f32x16 (&o)[D / 32], float& mref, float& lsum) {
+// Rows of one stage's segment that a 32-key sub-tile covers, and what masking needs.
+struct SubInfo {
+  int r;        // segment row of the sub-tile's first key
+  int slim;     // end of the segment's rows
+  int pdelta;   // global position of segment row x is pdelta + x (causal)
+};
+
+__device__ inline SubInfo sub_info(const KvCursor<64>& c, int sub) { return SubInfo{c.r + 32 * sub, c.slim, c.pdelta}; }
+
+// True when some entry of the sub-tile may be masked: it runs past its segment, or
+// (causal) its last key lies after the tile's first query.
+__device__ inline bool sub_needs_mask(const FwdArgs& a, const SubInfo& si, int qlo) {
+  return (si.r + 32 > si.slim) || (a.causal && si.pdelta + si.r + 31 > qlo);
+}
+
+// Set masked scores of a sub-tile to -inf. Lane (col, hf) holds keys 8*(e/4) + 4*hf + e%4.
+__device__ inline void mask_sub(const FwdArgs& a, const SubInfo& si, int hf, int qpos, f32x16& s) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = si.r + 8 * (e >> 2) + 4 * hf + (e & 3);
+    if (!(row < si.slim && (!a.causal || si.pdelta + row <= qpos))) s[e] = kNegInf;
+  }
+}
+
+// One step of the per-wave pipeline over 32-key sub-tiles (t = this step's softmax one):
+//   QK: sn = K Q^T for sub-tile t+1, K rows at kt (NKS MFMAs, one chain);
+//   PV: O^T += V^T P^T for sub-tile t-1, V rows at vt, P^T operands pp[0..1] (keys 0-15,
+//       16-31) (2*NDV MFMAs, one per value block and key half);
+//   SM: e = 2^(sc * S - ref) for sub-tile t (sc_ = S^T of t) and its lane sum ps.
+// Step i pairs QK k-step i with P.V product i and two (D = 128) or four (D = 64) of the
+// sixteen exponentials; LDS fragment reads run two steps ahead of their MFMAs. The
+// scheduling groups pin that interleave.
+template <int D, bool QK, bool PV, bool SM>
+__device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const bf16x8 (&qf)[D / 16],
+                                           const int (&koff)[D / 16], const int (&voff)[D / 32],
+                                           const bf16x8 (&pp)[2], f32x16 (&o)[D / 32], f32x16& sn,
+                                           const f32x16& sc_, float sc, float nm, f32x16& e, float& ps) {
   using L = Bf16Layout<D>;
-  constexpr int BN = L::BN, NKS = L::NKS, NDV = L::NDV;
-  const char* kt = cur_buf;
-  const char* vt = cur_buf + L::TILE;
-  const bool msk = cur.needs_mask(a, qlo);
+  constexpr int NKS = L::NKS, NDV = L::NDV;
+  static_assert(NKS == 2 * NDV, "one P.V product per QK k-step");
+  constexpr int EPS = 16 / NKS;                       // exponentials per step
+  constexpr int READS = (QK ? 1 : 0) + (PV ? 2 : 0);  // LDS reads per step
+  constexpr int AHEAD = 2;
+  bf16x8 kf[NKS];
+  s16x4 vlo[NKS], vhi[NKS];
+  auto load = [&](int i) {
+    if (QK) kf[i] = *reinterpret_cast<const bf16x8*>(kt + koff[i]);
+    if (PV) {
+      const int dv = i % NDV, ss = i / NDV;
+      const char* vb = vt + ss * 16 * L::ROWB;
+      vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[dv]));
+      vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * L::ROWB + voff[dv]));
+    }
+  };
 #pragma unroll
-  for (int sub = 0; sub < BN / 32; ++sub) {
-    // S^T = K Q^T for 32 keys x 32 queries.
-    bf16x8 kf[NKS];
+  for (int i = 0; i < AHEAD; ++i) load(i);
+  if (READS) __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * READS, 0);
+  if (QK) sn = f32x16{};
+  ps = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kt + sub * 32 * L::ROWB + koff[ks]);
-    f32x16 s = f32x16{};
+  for (int i = 0; i < NKS; ++i) {
+    if (i + AHEAD < NKS) load(i + AHEAD);
+    if (QK) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], sn, 0, 0, 0);
+    if (SM) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
-    if (msk) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int krow = cur.r + sub * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-        if (!cur.key_ok(a, krow, qpos)) s[e] = kNegInf;
+      for (int k = 0; k < EPS; ++k) {
+        const int x = EPS * i + k;
+        e[x] = fast_exp2(__builtin_fmaf(sc_[x], sc, nm));
+        ps += e[x];
       }
     }
-    // Online softmax, one query column per lane (two halves of 16 keys each).
-    // Fast path: exponentials against the current reference. Every p is positive, so a
-    // half-row whose sum stays within 2^kTau has every p within 2^kTau and needs no new
-    // reference. Otherwise -- a reference not yet set (-inf), or a score that passed it
-    // by more than kTau -- the wave takes the row maximum, raises the reference,
-    // rescales O and the sum, and recomputes p.
-    f32x16 p32;
-    float ps = 0.f;
-    {
-      const float nm = mref == kNegInf ? 0.f : -mref;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p32[e] = fast_exp2(__builtin_fmaf(s[e], sc, nm));
-        ps += p32[e];
-      }
+    if (PV) {
+      const int dv = i % NDV, ss = i / NDV;
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7));
+      o[dv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[ss], o[dv], 0, 0, 0);
     }
+    if (QK) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (SM) __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS / 2, 0);
+    if (PV) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (SM) __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS - 3 * EPS / 2, 0);
+    if (READS && i + AHEAD < NKS) __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+  }
+}
+
+// A full pipeline step: the masking of sub-tile t (when some of its entries may be
+// masked), the interleaved block, then the online-softmax update of sub-tile t and its
+// P^T operands. Fast path: exponentials against the current reference. Every p is
+// positive, so a lane whose 16-key sum stays within 2^kTau has every p within 2^kTau and
+// needs no new reference. Otherwise -- a reference not yet set (-inf), or a score that
+// passed it by more than kTau -- the wave takes the row maximum, raises the reference,
+// rescales O (which already holds the P.V products issued in this step, taken against
+// the old reference) and the sum, and recomputes p.
+template <int D, bool QK, bool PV, bool SM>
+__device__ __forceinline__ void pipe_step(const FwdArgs& a, const SubInfo& si, int hf, int qlo, int qpos, float sc,
+                                          const char* kt, const char* vt, const bf16x8 (&qf)[D / 16],
+                                          const int (&koff)[D / 16], const int (&voff)[D / 32],
+                                          const bf16x8 (&pp)[2], f32x16 (&o)[D / 32], f32x16& sn, f32x16& scur,
+                                          bf16x8 (&pc)[2], float& mref, float& lsum) {
+  constexpr int NDV = D / 32;
+  if (SM && sub_needs_mask(a, si, qlo)) mask_sub(a, si, hf, qpos, scur);
+  const float nm = mref == kNegInf ? 0.f : -mref;
+  f32x16 e;
+  float ps;
+  pipe_block<D, QK, PV, SM>(kt, vt, qf, koff, voff, pp, o, sn, scur, sc, nm, e, ps);
+  if (SM) {
     if (__builtin_amdgcn_ballot_w64(mref == kNegInf || ps > kBig)) {
-      float mx = s[0];
+      float mx = scur[0];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      for (int x = 1; x < 16; ++x) mx = fmaxf(mx, scur[x]);
       const float mn = fmaxf(mref, xhalf_max(mx) * sc);
       // 0 when only the old reference is -inf; 1 when both are (nothing seen yet)
       const float alpha = mn == kNegInf ? 1.f : fast_exp2(mref - mn);
@@ -305,37 +415,32 @@ __device__ __forceinline__ void fold_stage(
 #pragma unroll
       for (int dv = 0; dv < NDV; ++dv) o[dv] *= alpha;
       mref = mn;
-      const float nm = mref == kNegInf ? 0.f : -mref;
+      const float nm2 = mref == kNegInf ? 0.f : -mref;
       ps = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p32[e] = fast_exp2(__builtin_fmaf(s[e], sc, nm));
-        ps += p32[e];
+      for (int x = 0; x < 16; ++x) {
+        e[x] = fast_exp2(__builtin_fmaf(scur[x], sc, nm2));
+        ps += e[x];
       }
     }
     lsum += ps;
-    // O^T += V^T P^T, 16 keys per step.
-#pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      const bf16x8 p = to_bf16x8(p32, 8 * ss);
-      const char* vb = vt + (sub * 32 + ss * 16) * L::ROWB;
-#pragma unroll
-      for (int dv = 0; dv < NDV; ++dv) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[dv]));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * L::ROWB + voff[dv]));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p, o[dv], 0, 0, 0);
-      }
-    }
+    pc[0] = to_bf16x8(e, 0);
+    pc[1] = to_bf16x8(e, 8);
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   using L = Bf16Layout<D>;
-  constexpr int BN = L::BN, NKS = L::NKS, NDV = L::NDV;
-  __shared__ __attribute__((aligned(1024))) char smem0[L::STAGE];
-  __shared__ __attribute__((aligned(1024))) char smem1[L::STAGE];
+  constexpr int BN = L::BN, NKS = L::NKS, NDV = L::NDV, NB = L::NB;
+  static_assert(NB >= 4 && NB <= 6, "stage buffers");
+  __shared__ __attribute__((aligned(1024))) char sm0[L::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm1[L::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm2[L::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm3[L::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm4[NB > 4 ? L::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char sm5[NB > 5 ? L::STAGE : 16];
+  char* const bufs[6] = {sm0, sm1, sm2, sm3, sm4, sm5};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // Swizzled LDS byte offsets of this lane's fragments within a tile.
-  int koff[NKS];   // K fragment: row sub*32 + col, chunk 2*ks + hf
+  int koff[NKS];   // K fragment: row col (+ 32*sub), chunk 2*ks + hf
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) koff[ks] = col * L::ROWB + (((2 * ks + hf) ^ L::kswz(col)) << 4);
   int voff[NDV];   // V^T transpose read: row 4*(g/2) + i (+ 16*ss, + 8, + 32*sub)
@@ -391,32 +496,87 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const size_t blk_stride = (size_t)a.B * a.hkv * a.nkv * D;
   const size_t head_off = ((size_t)tile.b * a.hkv + tile.g) * a.nkv * D;
 
-  // Stages alternate between two LDS buffers. They are distinct arrays and the loop is
-  // unrolled over them, so the compiler can tell one stage's reads apart from the
-  // in-flight loads of the next (one shared array would make it wait for those loads
-  // before every LDS read). At each step: wait for this stage's own loads and the
-  // barrier (all waves' loads visible; the other buffer's old stage read by everyone),
-  // start streaming the next stage, then fold this one.
-  KvCursor<BN> c0, c1;
-  c0.begin(a, qhi);
-  if (c0.valid)
-    ld.issue(smem0, kg + c0.blk * blk_stride + head_off, vg + c0.blk * blk_stride + head_off, c0.r, a.nkv);
-  while (c0.valid) {
-    c1 = c0;
-    c1.next(a, qhi);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (c1.valid)
-      ld.issue(smem1, kg + c1.blk * blk_stride + head_off, vg + c1.blk * blk_stride + head_off, c1.r, a.nkv);
-    fold_stage<D>(a, c0, smem0, hf, qlo, qpos, sc, qf, koff, voff, o, mref, lsum);
-    if (!c1.valid) break;
-    c0 = c1;
-    c0.next(a, qhi);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (c0.valid)
-      ld.issue(smem0, kg + c0.blk * blk_stride + head_off, vg + c0.blk * blk_stride + head_off, c0.r, a.nkv);
-    fold_stage<D>(a, c1, smem1, hf, qlo, qpos, sc, qf, koff, voff, o, mref, lsum);
+  // Stage s lives in buffer s % NB and is read by the sub-tile steps 2s-1 and 2s (its K)
+  // and 2s+1 and 2s+2 (its V). Each stage begins with a workgroup barrier, before which
+  // every wave waits for its own loads of stage s: after it, stage s is complete in LDS
+  // for everyone, and stage s - 2 (last read at step 2s - 2) is free, so the loads of
+  // stage s + NB - 2 go into its buffer. The buffers are distinct arrays and the loop is
+  // unrolled over them, so the compiler can tell a stage's reads apart from the loads in
+  // flight into the other buffers. Even sub-tiles use (sA, pA), odd ones (sB, pB).
+  KvCursor<BN> lc, cc;   // next stage to load, stage being folded
+  lc.begin(a, qhi);
+  cc = lc;
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < NB - 2; ++s) {
+    if (lc.valid) {
+      ld.issue(bufs[s], kg + lc.blk * blk_stride + head_off, vg + lc.blk * blk_stride + head_off, lc.r, a.nkv);
+      lc.next(a, qhi);
+      ++issued;
+    }
+  }
+
+  if (cc.valid) {
+    f32x16 sA, sB;
+    bf16x8 pA[2], pB[2];
+    // ---- stage 0 (buffer 0): steps -1 and 0
+    wait_stages<D>(issued - 1);
+    phase_barrier();
+    if (lc.valid) {
+      ld.issue(bufs[NB - 2], kg + lc.blk * blk_stride + head_off, vg + lc.blk * blk_stride + head_off, lc.r, a.nkv);
+      lc.next(a, qhi);
+      ++issued;
+    }
+    SubInfo prev = sub_info(cc, 1);
+    pipe_step<D, true, false, false>(a, prev, hf, qlo, qpos, sc, bufs[0], bufs[0], qf, koff, voff, pB, o, sA, sB,
+                                     pB, mref, lsum);
+    pipe_step<D, true, false, true>(a, sub_info(cc, 0), hf, qlo, qpos, sc, bufs[0] + 32 * L::ROWB, bufs[0], qf,
+                                    koff, voff, pB, o, sB, sA, pA, mref, lsum);
+    cc.next(a, qhi);
+    int s = 1;
+    int last = 0;   // buffer of the last stage, for the tail
+    if (cc.valid) {
+      for (;;) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          // ---- stage s (buffer b); prev describes sub-tile 1 of stage s - 1 (buffer bp)
+          const int b = (1 + u) % NB, bp = u % NB;
+          wait_stages<D>(issued - (s + 1));
+          phase_barrier();
+          if (lc.valid) {
+            ld.issue(bufs[(1 + u + NB - 2) % NB], kg + lc.blk * blk_stride + head_off,
+                     vg + lc.blk * blk_stride + head_off, lc.r, a.nkv);
+            lc.next(a, qhi);
+            ++issued;
+          }
+          // step 2s-1: S of (s, sub 0); P.V of (s-1, sub 0); softmax of (s-1, sub 1)
+          pipe_step<D, true, true, true>(a, prev, hf, qlo, qpos, sc, bufs[b], bufs[bp] + L::TILE, qf, koff, voff,
+                                         pA, o, sA, sB, pB, mref, lsum);
+          // step 2s: S of (s, sub 1); P.V of (s-1, sub 1); softmax of (s, sub 0)
+          pipe_step<D, true, true, true>(a, sub_info(cc, 0), hf, qlo, qpos, sc, bufs[b] + 32 * L::ROWB,
+                                         bufs[bp] + L::TILE + 32 * L::ROWB, qf, koff, voff, pB, o, sB, sA, pA, mref,
+                                         lsum);
+          prev = sub_info(cc, 1);
+          cc.next(a, qhi);
+          ++s;
+          if (!cc.valid) {
+            last = b;
+            goto tail;
+          }
+        }
+      }
+    }
+  tail:
+    // ---- after the last stage (buffer `last`): steps 2n-1 and 2n
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b == last) {
+        pipe_step<D, false, true, true>(a, prev, hf, qlo, qpos, sc, bufs[b], bufs[b] + L::TILE, qf, koff, voff, pA,
+                                        o, sA, sB, pB, mref, lsum);
+        pipe_step<D, false, true, false>(a, prev, hf, qlo, qpos, sc, bufs[b], bufs[b] + L::TILE + 32 * L::ROWB, qf,
+                                         koff, voff, pB, o, sB, sA, pA, mref, lsum);
+      }
+    }
   }
 
   // Epilogue: out = O / sum, lse = ln(sum) + reference.
@@ -431,7 +591,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int i = 0; i < 4; ++i) {
       bf16x4 w;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = (__bf16)(o[dv][4 * i + j] * inv);
+      for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(o[dv][4 * i + jj] * inv);
       *reinterpret_cast<bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf) = w;
     }
   if (a.lse != nullptr && hf == 0) a.lse[ridx] = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
@@ -557,9 +717,9 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 
 hipError_t launch_forward_bf16(const FwdArgs& a, int grid, hipStream_t stream) {
   if (a.d == 128)
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(grid), dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -66,6 +66,10 @@ extern "C" int ra_rank_forward(const void* q, const void* k_blocks, const void* 
   if (is_zigzag && nkv % 2 != 0) return fail(RA_ERR_SHAPE, "zigzag needs an even nkv (got %d)", nkv);
   // Global positions (c * nkv tokens) and tile arithmetic stay in int32.
   if ((long long)c * nkv > INT_MAX / 2) return fail(RA_ERR_SHAPE, "sequence c*nkv=%lld too long", (long long)c * nkv);
+  // One (block, batch, KV head) slab of K or V is addressed with 32-bit byte offsets.
+  const long long elem_bytes = dtype == RA_BF16 ? 2 : 4;
+  if ((long long)nkv * head_dim * elem_bytes > INT_MAX)
+    return fail(RA_ERR_SHAPE, "nkv=%d rows of head_dim=%d exceed 2 GiB per KV head slab", nkv, head_dim);
   if (batch == 0 || nq == 0) return RA_OK;
 
   if (q == nullptr || out == nullptr) return fail(RA_ERR_ARG, "q and out must not be NULL");

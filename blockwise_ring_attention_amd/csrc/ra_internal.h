@@ -29,7 +29,7 @@ struct FwdArgs {
 };
 
 // Column blocks (of 32 query rows each) per workgroup, per kernel family.
-constexpr int kBf16ColBlocks = 4;   // 4 waves x 1 column block
+constexpr int kBf16ColBlocks = 8;   // 8 waves x 1 column block
 constexpr int kF32ColBlocks = 4;    // 4 waves x 1 column block
 
 hipError_t launch_forward_bf16(const FwdArgs& a, int grid, hipStream_t stream);

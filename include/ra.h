@@ -41,7 +41,9 @@ enum ra_status {
   RA_ERR_ARG = -1,         /* null pointer, c < 1, rank outside [0, c), hq % hkv != 0,
                               negative size, bad round range, unknown dtype */
   RA_ERR_SHAPE = -2,       /* causal with nq != nkv; causal zigzag with odd nkv;
-                              c * nkv above 2^30 tokens, or more than 2^31-1 tiles */
+                              c * nkv above 2^30 tokens, a KV head slab (nkv rows of
+                              head_dim elements) above 2^31-1 bytes, or more than
+                              2^31-1 tiles */
   RA_ERR_UNSUPPORTED = -3, /* (dtype, head_dim) pair not built: bf16 takes d = 64 or
                               128; fp32 takes d = 8, 16, ..., 128 */
   RA_ERR_ALIGN = -4,       /* a base pointer not 16-byte aligned */
