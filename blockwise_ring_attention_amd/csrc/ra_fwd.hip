@@ -198,12 +198,14 @@ struct Bf16Layout {
   static constexpr int ROWB = 2 * D;             // bytes per K or V row
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int TILE = BN * ROWB;         // bytes of one K (or V) tile
-  static constexpr int STAGE = 2 * TILE;         // K tile then V tile
-  static constexpr int NB = 5;                   // stage buffers (5 x 32 KiB = all LDS at D = 128)
+  static constexpr int NB = 4;                   // stage buffers: K tiles fill LDS [0, 64K), V tiles [64K, 128K) at D = 128
   static constexpr int RPL = 128 / D;            // rows per 256-byte bank line
   static constexpr int LOADS = TILE / (16 * 64 * WAVES);  // 16-byte loads per thread per tile
   static constexpr int NKS = D / 16;             // k-steps of QK^T per 32-key sub-tile
   static constexpr int NDV = D / 32;             // 32-wide blocks of the value dimension
+  // V tiles follow the NB K tiles in LDS; V^T fragment offsets carry this bias (see the
+  // kernel) so that a V tile address minus the bias fits the 16-bit read offset.
+  static constexpr int kVBias = NB * TILE >= 65536 ? 65536 : 0;
   static __device__ inline int kswz(int row) { return (row / RPL) & (CPR - 1); }
   static __device__ inline int vswz(int row) { return 4 * ((row / RPL) & (CPR / 4 - 1)); }
 };
@@ -237,7 +239,7 @@ struct StageLoader {
 
   // kb, vb: row 0 of the slab (nkv rows of 2*D bytes; nkv * 2 * D < 2^31 is checked on
   // the host).
-  __device__ inline void issue(char* stage, const __bf16* kb, const __bf16* vb, int r, int nkv) const {
+  __device__ inline void issue(char* kst, char* vst, const __bf16* kb, const __bf16* vb, int r, int nkv) const {
     typedef __attribute__((address_space(3))) void lds_void;
     const int bytes = nkv * L::ROWB;
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, bytes, kBufferFlags);
@@ -246,19 +248,19 @@ struct StageLoader {
     if (r + L::BN <= nkv) {
 #pragma unroll
       for (int u = 0; u < L::LOADS; ++u) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(stage + (u * L::WAVES + wave) * 1024), 16, koff[u],
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kst + (u * L::WAVES + wave) * 1024), 16, koff[u],
                                                  soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(stage + L::TILE + (u * L::WAVES + wave) * 1024), 16,
-                                                 voff[u], soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vst + (u * L::WAVES + wave) * 1024), 16, voff[u],
+                                                 soff, 0, 0);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < L::LOADS; ++u) {
         // rows past the slab repeat its last row (masked out by the fold)
         const int back = max(0, r + row[u] - (nkv - 1)) * L::ROWB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(stage + (u * L::WAVES + wave) * 1024), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kst + (u * L::WAVES + wave) * 1024), 16,
                                                  soff + (int)koff[u] - back, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(stage + L::TILE + (u * L::WAVES + wave) * 1024), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vst + (u * L::WAVES + wave) * 1024), 16,
                                                  soff + (int)voff[u] - back, 0, 0, 0);
       }
     }
@@ -348,7 +350,7 @@ __device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const
     if (QK) kf[i] = *reinterpret_cast<const bf16x8*>(kt + koff[i]);
     if (PV) {
       const int dv = i % NDV, ss = i / NDV;
-      const char* vb = vt + ss * 16 * L::ROWB;
+      const char* vb = vt - L::kVBias + ss * 16 * L::ROWB;   // voff carries +kVBias
       vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[dv]));
       vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * L::ROWB + voff[dv]));
     }
@@ -433,14 +435,17 @@ template <int D>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   using L = Bf16Layout<D>;
   constexpr int BN = L::BN, NKS = L::NKS, NDV = L::NDV, NB = L::NB;
-  static_assert(NB >= 4 && NB <= 6, "stage buffers");
-  __shared__ __attribute__((aligned(1024))) char sm0[L::STAGE];
-  __shared__ __attribute__((aligned(1024))) char sm1[L::STAGE];
-  __shared__ __attribute__((aligned(1024))) char sm2[L::STAGE];
-  __shared__ __attribute__((aligned(1024))) char sm3[L::STAGE];
-  __shared__ __attribute__((aligned(1024))) char sm4[NB > 4 ? L::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char sm5[NB > 5 ? L::STAGE : 16];
-  char* const bufs[6] = {sm0, sm1, sm2, sm3, sm4, sm5};
+  static_assert(NB == 4, "stage buffers");
+  __shared__ __attribute__((aligned(1024))) char k0[L::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1[L::TILE];
+  __shared__ __attribute__((aligned(1024))) char k2[L::TILE];
+  __shared__ __attribute__((aligned(1024))) char k3[L::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0[L::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1[L::TILE];
+  __shared__ __attribute__((aligned(1024))) char v2[L::TILE];
+  __shared__ __attribute__((aligned(1024))) char v3[L::TILE];
+  char* const kb[4] = {k0, k1, k2, k3};
+  char* const vb[4] = {v0, v1, v2, v3};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -482,7 +487,11 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int dv = 0; dv < NDV; ++dv) {
       const int chunk = 4 * dv + 2 * (g & 1) + (aa >> 1);
-      voff[dv] = vrow * L::ROWB + ((chunk ^ L::vswz(vrow)) << 4) + (aa & 1) * 8;
+      // Biased by kVBias, hidden from the compiler: V tiles sit above the 64 KiB reach of
+      // the ds_read offset field, and with the bias in the register each read addresses
+      // its tile as register + immediate instead of spending a VALU add per read.
+      voff[dv] = vrow * L::ROWB + ((chunk ^ L::vswz(vrow)) << 4) + (aa & 1) * 8 + L::kVBias;
+      asm volatile("" : "+v"(voff[dv]));
     }
   }
 
@@ -510,7 +519,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int s = 0; s < NB - 2; ++s) {
     if (lc.valid) {
-      ld.issue(bufs[s], kg + lc.blk * blk_stride + head_off, vg + lc.blk * blk_stride + head_off, lc.r, a.nkv);
+      ld.issue(kb[s], vb[s], kg + lc.blk * blk_stride + head_off, vg + lc.blk * blk_stride + head_off, lc.r, a.nkv);
       lc.next(a, qhi);
       ++issued;
     }
@@ -523,15 +532,16 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     wait_stages<D>(issued - 1);
     phase_barrier();
     if (lc.valid) {
-      ld.issue(bufs[NB - 2], kg + lc.blk * blk_stride + head_off, vg + lc.blk * blk_stride + head_off, lc.r, a.nkv);
+      ld.issue(kb[NB - 2], vb[NB - 2], kg + lc.blk * blk_stride + head_off, vg + lc.blk * blk_stride + head_off, lc.r,
+               a.nkv);
       lc.next(a, qhi);
       ++issued;
     }
     SubInfo prev = sub_info(cc, 1);
-    pipe_step<D, true, false, false>(a, prev, hf, qlo, qpos, sc, bufs[0], bufs[0], qf, koff, voff, pB, o, sA, sB,
-                                     pB, mref, lsum);
-    pipe_step<D, true, false, true>(a, sub_info(cc, 0), hf, qlo, qpos, sc, bufs[0] + 32 * L::ROWB, bufs[0], qf,
-                                    koff, voff, pB, o, sB, sA, pA, mref, lsum);
+    pipe_step<D, true, false, false>(a, prev, hf, qlo, qpos, sc, kb[0], vb[0], qf, koff, voff, pB, o, sA, sB, pB,
+                                     mref, lsum);
+    pipe_step<D, true, false, true>(a, sub_info(cc, 0), hf, qlo, qpos, sc, kb[0] + 32 * L::ROWB, vb[0], qf, koff,
+                                    voff, pB, o, sB, sA, pA, mref, lsum);
     cc.next(a, qhi);
     int s = 1;
     int last = 0;   // buffer of the last stage, for the tail
@@ -544,18 +554,17 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
           wait_stages<D>(issued - (s + 1));
           phase_barrier();
           if (lc.valid) {
-            ld.issue(bufs[(1 + u + NB - 2) % NB], kg + lc.blk * blk_stride + head_off,
+            ld.issue(kb[(1 + u + NB - 2) % NB], vb[(1 + u + NB - 2) % NB], kg + lc.blk * blk_stride + head_off,
                      vg + lc.blk * blk_stride + head_off, lc.r, a.nkv);
             lc.next(a, qhi);
             ++issued;
           }
           // step 2s-1: S of (s, sub 0); P.V of (s-1, sub 0); softmax of (s-1, sub 1)
-          pipe_step<D, true, true, true>(a, prev, hf, qlo, qpos, sc, bufs[b], bufs[bp] + L::TILE, qf, koff, voff,
-                                         pA, o, sA, sB, pB, mref, lsum);
+          pipe_step<D, true, true, true>(a, prev, hf, qlo, qpos, sc, kb[b], vb[bp], qf, koff, voff, pA, o, sA, sB, pB,
+                                         mref, lsum);
           // step 2s: S of (s, sub 1); P.V of (s-1, sub 1); softmax of (s, sub 0)
-          pipe_step<D, true, true, true>(a, sub_info(cc, 0), hf, qlo, qpos, sc, bufs[b] + 32 * L::ROWB,
-                                         bufs[bp] + L::TILE + 32 * L::ROWB, qf, koff, voff, pB, o, sB, sA, pA, mref,
-                                         lsum);
+          pipe_step<D, true, true, true>(a, sub_info(cc, 0), hf, qlo, qpos, sc, kb[b] + 32 * L::ROWB,
+                                         vb[bp] + 32 * L::ROWB, qf, koff, voff, pB, o, sB, sA, pA, mref, lsum);
           prev = sub_info(cc, 1);
           cc.next(a, qhi);
           ++s;
@@ -571,10 +580,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (b == last) {
-        pipe_step<D, false, true, true>(a, prev, hf, qlo, qpos, sc, bufs[b], bufs[b] + L::TILE, qf, koff, voff, pA,
-                                        o, sA, sB, pB, mref, lsum);
-        pipe_step<D, false, true, false>(a, prev, hf, qlo, qpos, sc, bufs[b], bufs[b] + L::TILE + 32 * L::ROWB, qf,
-                                         koff, voff, pB, o, sB, sA, pA, mref, lsum);
+        pipe_step<D, false, true, true>(a, prev, hf, qlo, qpos, sc, kb[b], vb[b], qf, koff, voff, pA, o, sA, sB, pB,
+                                        mref, lsum);
+        pipe_step<D, false, true, false>(a, prev, hf, qlo, qpos, sc, kb[b], vb[b] + 32 * L::ROWB, qf, koff, voff, pB,
+                                         o, sB, sA, pA, mref, lsum);
       }
     }
   }
