@@ -38,6 +38,9 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kTau = 8.0f;
 constexpr float kBig = 256.0f;   // 2^kTau
 constexpr float kLn2 = 0.693147180559945309f;
+// Initial exponent reference of the bf16 fold: finite, far below any finite scaled score,
+// so the first unmasked exponential overflows and raises the reference (see pipe_step).
+constexpr float kRef0 = -1.0e30f;
 // Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: 32-bit data format,
 // no swizzle; accesses at or past num_records bytes are out of range.
 constexpr int kBufferFlags = 0x00020000;
@@ -99,9 +102,10 @@ __device__ inline int query_pos(const FwdArgs& a, int t) {
 template <int BN>
 struct KvCursor {
   int t, seg, r, rend, slim, pdelta, blk;
+  int mrow;    // a 32-key run starting at segment row x may hold masked entries iff x > mrow
   int valid;   // int, not bool: keeps the struct a plain array of words that SROA splits
 
-  __device__ inline bool enter(const FwdArgs& a, int qhi) {
+  __device__ inline bool enter(const FwdArgs& a, int qlo, int qhi) {
     blk = a.rank - t;
     if (blk < 0) blk += a.c;
     int r0;
@@ -116,35 +120,34 @@ struct KvCursor {
       r0 = 0; slim = a.nkv; pdelta = a.causal ? blk * a.nkv : 0;
     }
     rend = slim;
+    // A run [x, x+32) needs a mask when it passes the segment's end, or (causal) when its
+    // last key lies after the tile's first query.
+    mrow = slim - 32;
     if (a.causal) {
       const int lim = qhi - pdelta + 1;   // rows whose position <= qhi
       rend = max(r0, min(rend, lim));
+      mrow = min(mrow, qlo - pdelta - 31);
     }
     r = r0;
     return r < rend;
   }
-  __device__ inline void seek(const FwdArgs& a, int qhi) {
+  __device__ inline void seek(const FwdArgs& a, int qlo, int qhi) {
     const int nseg = (a.causal && a.zigzag) ? 2 : 1;
     while (t < a.t1) {
-      if (enter(a, qhi)) { valid = 1; return; }
+      if (enter(a, qlo, qhi)) { valid = 1; return; }
       if (++seg == nseg) { seg = 0; ++t; }
     }
     valid = 0;
   }
-  __device__ inline void begin(const FwdArgs& a, int qhi) {
-    t = a.t0; seg = 0; seek(a, qhi);
+  __device__ inline void begin(const FwdArgs& a, int qlo, int qhi) {
+    t = a.t0; seg = 0; seek(a, qlo, qhi);
   }
-  __device__ inline void next(const FwdArgs& a, int qhi) {
+  __device__ inline void next(const FwdArgs& a, int qlo, int qhi) {
     r += BN;
     if (r < rend) return;
     const int nseg = (a.causal && a.zigzag) ? 2 : 1;
     if (++seg == nseg) { seg = 0; ++t; }
-    seek(a, qhi);
-  }
-  // True when some entry of the tile may be masked: it runs past its segment, or (causal)
-  // its last key lies after the tile's first query.
-  __device__ inline bool needs_mask(const FwdArgs& a, int qlo) const {
-    return (r + BN > slim) || (a.causal && pdelta + r + BN - 1 > qlo);
+    seek(a, qlo, qhi);
   }
   __device__ inline bool key_ok(const FwdArgs& a, int row, int qpos) const {
     return row < slim && (!a.causal || pdelta + row <= qpos);
@@ -306,14 +309,12 @@ struct SubInfo {
   int r;        // segment row of the sub-tile's first key
   int slim;     // end of the segment's rows
   int pdelta;   // global position of segment row x is pdelta + x (causal)
+  int mask;     // some entry may be masked (see KvCursor::mrow)
 };
 
-__device__ inline SubInfo sub_info(const KvCursor<64>& c, int sub) { return SubInfo{c.r + 32 * sub, c.slim, c.pdelta}; }
-
-// True when some entry of the sub-tile may be masked: it runs past its segment, or
-// (causal) its last key lies after the tile's first query.
-__device__ inline bool sub_needs_mask(const FwdArgs& a, const SubInfo& si, int qlo) {
-  return (si.r + 32 > si.slim) || (a.causal && si.pdelta + si.r + 31 > qlo);
+__device__ inline SubInfo sub_info(const KvCursor<64>& c, int sub) {
+  const int r = c.r + 32 * sub;
+  return SubInfo{r, c.slim, c.pdelta, r > c.mrow};
 }
 
 // Set masked scores of a sub-tile to -inf. Lane (col, hf) holds keys 8*(e/4) + 4*hf + e%4.
@@ -389,10 +390,11 @@ __device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const
 // masked), the interleaved block, then the online-softmax update of sub-tile t and its
 // P^T operands. Fast path: exponentials against the current reference. Every p is
 // positive, so a lane whose 16-key sum stays within 2^kTau has every p within 2^kTau and
-// needs no new reference. Otherwise -- a reference not yet set (-inf), or a score that
-// passed it by more than kTau -- the wave takes the row maximum, raises the reference,
+// needs no new reference. Otherwise -- a score that passed the reference by more than
+// kTau, which includes the first unmasked score against the initial reference kRef0,
+// whose exponential overflows -- the wave takes the row maximum, raises the reference,
 // rescales O (which already holds the P.V products issued in this step, taken against
-// the old reference) and the sum, and recomputes p.
+// the old reference) and the sum, and recomputes p. Masked scores are -inf and give 0.
 template <int D, bool QK, bool PV, bool SM>
 __device__ __forceinline__ void pipe_step(const FwdArgs& a, const SubInfo& si, int hf, int qlo, int qpos, float sc,
                                           const char* kt, const char* vt, const bf16x8 (&qf)[D / 16],
@@ -400,24 +402,24 @@ __device__ __forceinline__ void pipe_step(const FwdArgs& a, const SubInfo& si, i
                                           const bf16x8 (&pp)[2], f32x16 (&o)[D / 32], f32x16& sn, f32x16& scur,
                                           bf16x8 (&pc)[2], float& mref, float& lsum) {
   constexpr int NDV = D / 32;
-  if (SM && sub_needs_mask(a, si, qlo)) mask_sub(a, si, hf, qpos, scur);
-  const float nm = mref == kNegInf ? 0.f : -mref;
+  if (SM && si.mask) mask_sub(a, si, hf, qpos, scur);
+  const float nm = -mref;
   f32x16 e;
   float ps;
   pipe_block<D, QK, PV, SM>(kt, vt, qf, koff, voff, pp, o, sn, scur, sc, nm, e, ps);
   if (SM) {
-    if (__builtin_amdgcn_ballot_w64(mref == kNegInf || ps > kBig)) {
+    if (__builtin_amdgcn_ballot_w64(ps > kBig)) {
       float mx = scur[0];
 #pragma unroll
       for (int x = 1; x < 16; ++x) mx = fmaxf(mx, scur[x]);
+      // mn >= mref stays finite; alpha is 0 when the old reference was the initial one
       const float mn = fmaxf(mref, xhalf_max(mx) * sc);
-      // 0 when only the old reference is -inf; 1 when both are (nothing seen yet)
-      const float alpha = mn == kNegInf ? 1.f : fast_exp2(mref - mn);
+      const float alpha = fast_exp2(mref - mn);
       lsum *= alpha;
 #pragma unroll
       for (int dv = 0; dv < NDV; ++dv) o[dv] *= alpha;
       mref = mn;
-      const float nm2 = mref == kNegInf ? 0.f : -mref;
+      const float nm2 = -mref;
       ps = 0.f;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
@@ -498,12 +500,24 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   f32x16 o[NDV];
 #pragma unroll
   for (int dv = 0; dv < NDV; ++dv) o[dv] = f32x16{};
-  float mref = kNegInf;   // exponent reference, log2 units
+  float mref = kRef0;     // exponent reference, log2 units
   float lsum = 0.f;       // this half's share of the running sum
   const float sc = a.scale_log2;
 
   const size_t blk_stride = (size_t)a.B * a.hkv * a.nkv * D;
   const size_t head_off = ((size_t)tile.b * a.hkv + tile.g) * a.nkv * D;
+  // K/V slab of the block being loaded, recomputed only when the block changes.
+  int slab_blk = -1;
+  const __bf16* kslab = kg;
+  const __bf16* vslab = vg;
+  auto issue = [&](char* kst, char* vst, const KvCursor<BN>& c) {
+    if (c.blk != slab_blk) {
+      slab_blk = c.blk;
+      kslab = kg + slab_blk * blk_stride + head_off;
+      vslab = vg + slab_blk * blk_stride + head_off;
+    }
+    ld.issue(kst, vst, kslab, vslab, c.r, a.nkv);
+  };
 
   // Stage s lives in buffer s % NB and is read by the sub-tile steps 2s-1 and 2s (its K)
   // and 2s+1 and 2s+2 (its V). Each stage begins with a workgroup barrier, before which
@@ -513,14 +527,14 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // unrolled over them, so the compiler can tell a stage's reads apart from the loads in
   // flight into the other buffers. Even sub-tiles use (sA, pA), odd ones (sB, pB).
   KvCursor<BN> lc, cc;   // next stage to load, stage being folded
-  lc.begin(a, qhi);
+  lc.begin(a, qlo, qhi);
   cc = lc;
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < NB - 2; ++s) {
     if (lc.valid) {
-      ld.issue(kb[s], vb[s], kg + lc.blk * blk_stride + head_off, vg + lc.blk * blk_stride + head_off, lc.r, a.nkv);
-      lc.next(a, qhi);
+      issue(kb[s], vb[s], lc);
+      lc.next(a, qlo, qhi);
       ++issued;
     }
   }
@@ -532,9 +546,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     wait_stages<D>(issued - 1);
     phase_barrier();
     if (lc.valid) {
-      ld.issue(kb[NB - 2], vb[NB - 2], kg + lc.blk * blk_stride + head_off, vg + lc.blk * blk_stride + head_off, lc.r,
-               a.nkv);
-      lc.next(a, qhi);
+      issue(kb[NB - 2], vb[NB - 2], lc);
+      lc.next(a, qlo, qhi);
       ++issued;
     }
     SubInfo prev = sub_info(cc, 1);
@@ -542,7 +555,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
                                      mref, lsum);
     pipe_step<D, true, false, true>(a, sub_info(cc, 0), hf, qlo, qpos, sc, kb[0] + 32 * L::ROWB, vb[0], qf, koff,
                                     voff, pB, o, sB, sA, pA, mref, lsum);
-    cc.next(a, qhi);
+    cc.next(a, qlo, qhi);
     int s = 1;
     int last = 0;   // buffer of the last stage, for the tail
     if (cc.valid) {
@@ -554,9 +567,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
           wait_stages<D>(issued - (s + 1));
           phase_barrier();
           if (lc.valid) {
-            ld.issue(kb[(1 + u + NB - 2) % NB], vb[(1 + u + NB - 2) % NB], kg + lc.blk * blk_stride + head_off,
-                     vg + lc.blk * blk_stride + head_off, lc.r, a.nkv);
-            lc.next(a, qhi);
+            issue(kb[(1 + u + NB - 2) % NB], vb[(1 + u + NB - 2) % NB], lc);
+            lc.next(a, qlo, qhi);
             ++issued;
           }
           // step 2s-1: S of (s, sub 0); P.V of (s-1, sub 0); softmax of (s-1, sub 1)
@@ -566,7 +578,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
           pipe_step<D, true, true, true>(a, sub_info(cc, 0), hf, qlo, qpos, sc, kb[b] + 32 * L::ROWB,
                                          vb[bp] + 32 * L::ROWB, qf, koff, voff, pB, o, sB, sA, pA, mref, lsum);
           prev = sub_info(cc, 1);
-          cc.next(a, qhi);
+          cc.next(a, qlo, qhi);
           ++s;
           if (!cc.valid) {
             last = b;
@@ -649,7 +661,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   const size_t head_off = ((size_t)tile.b * a.hkv + tile.g) * a.nkv * d;
 
   KvCursor<BN> cur;
-  cur.begin(a, qhi);
+  cur.begin(a, qlo, qhi);
   while (cur.valid) {
     __syncthreads();
     const float* kb = kg + cur.blk * blk_stride + head_off;
@@ -666,7 +678,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < DP / 2; ++ks)
       if (2 * ks < d) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kl[col * KSF + 2 * ks + hf], qf[ks], s, 0, 0, 0);
-    if (cur.needs_mask(a, qlo)) {
+    if (cur.r > cur.mrow) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int krow = cur.r + 8 * (e >> 2) + 4 * hf + (e & 3);
@@ -700,7 +712,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
           o[dv] = __builtin_amdgcn_mfma_f32_32x32x2f32(vl[(8 * (e >> 2) + 4 * hf + (e & 3)) * VSF + 32 * dv + col],
                                                        s[e], o[dv], 0, 0, 0);
       }
-    cur.next(a, qhi);
+    cur.next(a, qlo, qhi);
   }
 
   const float lt = xhalf_sum(lsum);
