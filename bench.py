@@ -1,11 +1,14 @@
 """Throughput of one rank's share of Ring Attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-also] [--no-per-round] [--balance]
 
 One step = one fused launch of ra_rank_forward over the whole share (all c ring rounds,
 causal skipping, GQA, lse) on seeded synthetic inputs already resident in HBM. The value
 is unmasked TFLOP/s: 4*d FLOP per allowed score entry over the step time. Prints one
-JSON line.
+JSON line; it also carries the streamed form of the same share (one launch per ring
+round merged with ra_merge, "per_round"). ``--balance`` instead times every rank of the
+workload with contiguous and with zigzag chunks and prints that sweep.
 """
 
 from __future__ import annotations
@@ -58,13 +61,7 @@ def workload_numbers(w):
 def time_workload(w, steps: int, warmup: int, arrays=None):
     import torch
     import blockwise_ring_attention_amd as ra
-    from blockwise_ring_attention_amd.inputs import make_inputs
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    q, k, v = arrays if arrays is not None else make_inputs(w)
-    qd = torch.from_numpy(q).to("cuda", dt)
-    kd = torch.from_numpy(k).to("cuda", dt)
-    vd = torch.from_numpy(v).to("cuda", dt)
-    del q, k, v
+    qd, kd, vd = _device_inputs(w, arrays)
     out = torch.empty_like(qd)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda") if w.with_lse else None
 
@@ -89,6 +86,108 @@ def time_workload(w, steps: int, warmup: int, arrays=None):
     del qd, kd, vd, out, lse
     torch.cuda.empty_cache()
     return wall / steps * 1e3, sum(launch_ms) / len(launch_ms), min(launch_ms)
+
+
+def _device_inputs(w, arrays):
+    import torch
+    from blockwise_ring_attention_amd.inputs import make_inputs
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = arrays if arrays is not None else make_inputs(w)
+    return (torch.from_numpy(q).to("cuda", dt), torch.from_numpy(k).to("cuda", dt),
+            torch.from_numpy(v).to("cuda", dt))
+
+
+def time_per_round(w, steps: int, warmup: int, arrays=None):
+    """The streamed form of the same share, as a live ring rank runs it: one launch per
+    ring round (rounds [t, t+1)), each partial merged with ra_merge into the running
+    (out, lse) kept in HBM (in place, in the input dtype). One step = all c rounds.
+    Returns step ms, per-round kernel ms, per-merge ms (from one event-instrumented
+    step), and the max abs difference of the merged result from the fused launch."""
+    import torch
+    import blockwise_ring_attention_amd as ra
+    qd, kd, vd = _device_inputs(w, arrays)
+    acc = torch.empty_like(qd)
+    acc_lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
+    part = torch.empty_like(qd)
+    part_lse = torch.empty_like(acc_lse)
+    c = w.c
+
+    def launch(t):
+        if t == 0:
+            ra.rank_forward(qd, kd, vd, c, w.rank, w.causal, w.zigzag, 0, 1, out=acc, lse=acc_lse)
+        else:
+            ra.rank_forward(qd, kd, vd, c, w.rank, w.causal, w.zigzag, t, t + 1, out=part, lse=part_lse)
+
+    def merge():
+        ra.merge(acc, acc_lse, part, part_lse, out=acc, lse=acc_lse)
+
+    def step():
+        for t in range(c):
+            launch(t)
+            if t > 0:
+                merge()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    # one instrumented step: an event pair around every launch and every merge
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(c)]
+    for t in range(c):
+        ev[t][0].record(stream)
+        launch(t)
+        ev[t][1].record(stream)
+        if t > 0:
+            ev[t][2].record(stream)
+            merge()
+            ev[t][3].record(stream)
+    torch.cuda.synchronize()
+    round_ms = [ev[t][0].elapsed_time(ev[t][1]) for t in range(c)]
+    merge_ms = [ev[t][2].elapsed_time(ev[t][3]) for t in range(1, c)]
+    fused, fused_lse = ra.rank_forward(qd, kd, vd, c, w.rank, w.causal, w.zigzag, with_lse=True)
+    torch.cuda.synchronize()
+    diff = (acc.float() - fused.float()).abs().max().item()
+    fin = torch.isfinite(fused_lse)
+    lse_diff = (acc_lse[fin] - fused_lse[fin]).abs().max().item() if bool(fin.any()) else 0.0
+    del qd, kd, vd, acc, acc_lse, part, part_lse, fused, fused_lse
+    torch.cuda.empty_cache()
+    return ms_step, round_ms, merge_ms, diff, lse_diff
+
+
+def balance_sweep(w, steps: int, warmup: int):
+    """Every rank r = 0..c-1 of the workload, once with contiguous chunks and once with
+    the zigzag pairing (causal), each a fused launch: ms per rank and the spread. Q is the
+    same array for every rank (its values do not change the work)."""
+    import dataclasses
+    import torch
+    from blockwise_ring_attention_amd import accounting as acc
+    from blockwise_ring_attention_amd.inputs import make_inputs
+    arrays = make_inputs(w)
+    res = {}
+    for zig in (False, True):
+        ranks = []
+        for r in range(w.c):
+            wr = dataclasses.replace(w, rank=r, zigzag=zig)
+            ms, ml, mn = time_workload(wr, steps, warmup, arrays)
+            e = acc.allowed_entries(w.c, r, w.rows, w.rows, True, zig)
+            flop = acc.unmasked_flop(w.batch, w.hq, w.head_dim, e)
+            units = sum(1 for j in range(w.c) if acc.block_allowed(w.c, r, j, w.rows, w.rows, True, zig) > 0)
+            ranks.append({"rank": r, "kernel_ms": round(ml, 4), "tflops": round(flop / (ml * 1e-3) / 1e12, 1),
+                          "allowed_entries_per_head": e, "kv_blocks_with_work": units})
+        times = [x["kernel_ms"] for x in ranks]
+        res["zigzag" if zig else "contiguous"] = {
+            "ranks": ranks, "max_ms": max(times), "min_ms": min(times),
+            "max_over_min": round(max(times) / min(times), 3),
+            "ring_round_ms_bound": round(max(times), 4)}
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, arrays, min_seconds: float = 10.0):
@@ -150,6 +249,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--no-per-round", action="store_true",
+                    help="skip the streamed form (one launch per ring round plus ra_merge)")
+    ap.add_argument("--balance", action="store_true",
+                    help="only run the all-rank sweep (contiguous vs zigzag chunks) of the workload and print it")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum length of the timed oracle run for cpu_baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -178,6 +281,11 @@ def main():
         build.build()
     from blockwise_ring_attention_amd.inputs import make_inputs
     w = WORKLOADS[args.workload]
+    if args.balance:
+        sweep = balance_sweep(w, args.steps, args.warmup)
+        print(json.dumps({"balance_sweep": w.name, "c": w.c, "seq": w.seq, "steps": args.steps,
+                          "warmup": args.warmup, **sweep}), flush=True)
+        return
     flop, nbytes = workload_numbers(w)
     arrays = make_inputs(w)
     ms_step, ms_launch, ms_min = time_workload(w, args.steps, args.warmup, arrays)
@@ -217,6 +325,14 @@ def main():
             also.append({"workload": name, "value": round(fa / (ms_a * 1e-3) / 1e12, 2), "ms_per_step": round(ms_a, 4),
                          "pct_of_peak": round(100 * fa / (ms_a * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)})
         line["also"] = also
+    if not args.no_per_round:
+        ms_pr, round_ms, merge_ms, diff, lse_diff = time_per_round(w, max(1, args.steps // 4), 1, arrays)
+        line["per_round"] = {
+            "what": "one launch per ring round (rounds [t, t+1)) + in-place ra_merge into the running (out, lse)",
+            "ms_per_step": round(ms_pr, 4), "value": round(flop / (ms_pr * 1e-3) / 1e12, 2),
+            "overhead_vs_fused": round(ms_pr / ms_step - 1.0, 4),
+            "round_kernel_ms": [round(x, 4) for x in round_ms], "merge_ms": [round(x, 4) for x in merge_ms],
+            "max_abs_diff_vs_fused": diff, "lse_max_abs_diff_vs_fused": lse_diff}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, arrays, args.cpu_seconds)
     torch.cuda.synchronize()
