@@ -38,6 +38,8 @@ class Workload:
     seed: int
     key_outlier_frac: float = 0.0   # fraction of key rows redrawn per (b, kv head)
     key_outlier_std: float = 0.0
+    doc_median: int = 0             # > 0: packed documents, lognormal lengths with this median
+    doc_sigma: float = 0.0
     with_lse: bool = True
     notes: str = field(default="", compare=False)
 
@@ -62,6 +64,9 @@ WORKLOADS = {
         Workload("mha16_b2_d128_s64k_c8_noncausal_outliers_bf16", "bf16", 2, 16, 16, 128, 65536, 8, 0, False, False,
                  1.0, 4, key_outlier_frac=0.01, key_outlier_std=3.0,
                  notes="1% of key rows per (b, head) redrawn from N(0, 3^2)"),
+        Workload("gqa64x8_d128_s128k_c16_zigzag_docs_bf16", "bf16", 1, 64, 8, 128, 131072, 16, 0, True, True, 0.5, 3,
+                 doc_median=8192, doc_sigma=1.0,
+                 notes="the 128k share with a packed-document mask: lognormal document lengths, median 8192"),
     ]
 }
 
@@ -96,6 +101,40 @@ def make_inputs(w: Workload, seed: int | None = None, rows: int | None = None):
                 vals = rng.standard_normal((count, w.head_dim), dtype=np.float32) * np.float32(w.key_outlier_std)
                 k[idx // n, b, g, idx % n] = vals
     return round_to_dtype(q, w.dtype), round_to_dtype(k, w.dtype), round_to_dtype(v, w.dtype)
+
+
+def doc_start_from_lengths(lengths) -> np.ndarray:
+    """The doc_start array of a packed sequence whose documents have ``lengths`` tokens,
+    in order: entry p is the position where p's document begins (int32)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    if np.any(lengths < 1):
+        raise ValueError("document lengths must be positive")
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+    return np.repeat(starts, lengths).astype(np.int32)
+
+
+def draw_document_lengths(total: int, median: float, sigma: float, seed) -> np.ndarray:
+    """Seeded lognormal document lengths (at least 1 token) packed into ``total`` tokens;
+    the last document is cut to fit."""
+    rng = np.random.default_rng(seed)
+    lengths = []
+    used = 0
+    while used < total:
+        n = max(1, int(round(float(rng.lognormal(np.log(median), sigma)))))
+        n = min(n, total - used)
+        lengths.append(n)
+        used += n
+    return np.asarray(lengths, dtype=np.int64)
+
+
+def make_doc_start(w: Workload, rows: int | None = None):
+    """The workload's document layout as a doc_start array over all c * n positions, or
+    None when it has no document mask. Drawn from its own stream (seed, 1), so Q/K/V stay
+    those of the same workload without documents."""
+    if w.doc_median <= 0:
+        return None
+    n = w.rows if rows is None else rows
+    return doc_start_from_lengths(draw_document_lengths(w.c * n, w.doc_median, w.doc_sigma, [w.seed, 1]))
 
 
 def random_array(shape, dtype: str, seed: int, scale: float = 1.0) -> np.ndarray:

@@ -12,6 +12,10 @@ Functions and their pins (the tests that tie each one to something other than it
   blockwise fold in any block order; torch's fp64 scaled-dot-product attention with
   ``enable_gqa`` on the full sequence; gathering rank rows out of full-sequence causal
   attention; closed forms (Q = 0, constant V, key shift).
+* ``attention.rank_forward(..., doc_start=...)`` -- the document mask of packed
+  sequences. Pinned by: torch's fp64 causal attention run separately on every document
+  span; 50-digit brute force; all-zero starts reduce to the causal mask; shares gathered
+  out of the full sequence; the Q = 0 closed form (lse = ln of the document prefix).
 * ``attention.merge`` -- combination of two partial results. Pinned by: merging results
   over disjoint key sets equals the oracle over their union; identity and symmetry.
 * ``fold.online_softmax_fold`` -- the online-softmax update, a second implementation
@@ -29,6 +33,7 @@ from .attention import (  # noqa: F401
     allowed_count,
     chunk_positions,
     chunk_units,
+    document_allowed,
     kv_head,
     merge,
     rank_forward,

@@ -29,6 +29,12 @@ What is computed, and where it is stated:
   KV head ``h // (Hq / Hkv)``.
 * Log-sum-exp per row: ``lse = ln sum_allowed exp(s)`` of the scaled scores, natural
   log; ``-inf`` (with output 0) for a row with no allowed key.
+* Document mask: in a packed sequence, attention must not cross document boundaries
+  ("What do you do about long sequences and sparse models?", section "Why did Llama 3
+  not use a ring?"). Reading taken: documents are contiguous spans; ``doc_start[p]`` is
+  the global position where p's document begins (so it also identifies the document),
+  and the query at p sees exactly the keys at positions x with doc_start[p] <= x <= p.
+  Values of ``doc_start`` are taken as given (a value above p leaves the row empty).
 """
 
 from __future__ import annotations
@@ -48,6 +54,13 @@ def causal_allowed(pos_q: np.ndarray, pos_k: np.ndarray) -> np.ndarray:
     """[len(pos_q), len(pos_k)] mask of the causal rule: key j is visible to query i iff
     j <= i ("Context parallelism: splitting the sequence")."""
     return pos_k[None, :] <= pos_q[:, None]
+
+
+def document_allowed(pos_q: np.ndarray, pos_k: np.ndarray, doc_start) -> np.ndarray:
+    """[len(pos_q), len(pos_k)] mask of the causal document rule: the query at p sees the
+    key at x iff doc_start[p] <= x <= p (its own document, up to itself)."""
+    lo = np.asarray(doc_start, dtype=np.int64)[pos_q]
+    return (pos_k[None, :] <= pos_q[:, None]) & (pos_k[None, :] >= lo[:, None])
 
 
 def kv_head(h: int, hq: int, hkv: int) -> int:
@@ -102,7 +115,7 @@ def _row_attention(qrows, kall, vall, allowed, scale):
 
 
 def rank_forward(q, k_blocks, v_blocks, c: int, rank: int, causal: bool, zigzag: bool,
-                 round_begin: int = 0, round_end: int | None = None, rows=None):
+                 round_begin: int = 0, round_end: int | None = None, rows=None, doc_start=None):
     """Oracle for one rank's share: attention of the rank's queries over the keys of the
     KV blocks it folds in during rounds [round_begin, round_end) (all c rounds by
     default, which is the full row).
@@ -111,6 +124,8 @@ def rank_forward(q, k_blocks, v_blocks, c: int, rank: int, causal: bool, zigzag:
     k_blocks [c, B, Hkv, n, d]   KV block j = rank j's keys, in owner order
     v_blocks [c, B, Hkv, n, dv]
     rows     optional int array [R, 3] of (b, h, t) triples: compute only those rows.
+    doc_start optional int array [c * n] by global position (causal only): the document
+             mask, keys at doc_start[p] <= x <= p for the query at p.
 
     Returns (out, lse): out [B, Hq, Nq, dv] fp64 and lse [B, Hq, Nq] fp64 when rows is
     None, else out [R, dv] and lse [R] in the order of ``rows``.
@@ -126,6 +141,12 @@ def rank_forward(q, k_blocks, v_blocks, c: int, rank: int, causal: bool, zigzag:
         raise ValueError("Hq must be a multiple of Hkv")
     if causal and nq != n:
         raise ValueError("causal needs as many query rows as KV rows per block")
+    if doc_start is not None:
+        if not causal:
+            raise ValueError("the document mask is causal")
+        doc_start = np.asarray(doc_start, dtype=np.int64)
+        if doc_start.shape != (c * n,):
+            raise ValueError("doc_start needs one entry per global position (c * n)")
     dv = v_blocks.shape[4]
     scale = score_scale(d)
 
@@ -150,7 +171,9 @@ def rank_forward(q, k_blocks, v_blocks, c: int, rank: int, causal: bool, zigzag:
         step = max(1, _SCORE_BUDGET // max(1, kall.shape[0]))
         for i in range(0, len(ts), step):
             tt = ts[i:i + step]
-            if causal:
+            if doc_start is not None:
+                allowed = document_allowed(pos_q[tt], pos_k, doc_start)
+            elif causal:
                 allowed = causal_allowed(pos_q[tt], pos_k)
             else:
                 allowed = np.ones((len(tt), kall.shape[0]), dtype=bool)
@@ -208,7 +231,7 @@ def merge(out_a, lse_a, out_b, lse_b):
 
 
 def allowed_count(c: int, rank: int, rows: int, causal: bool, zigzag: bool,
-                  round_begin: int = 0, round_end: int | None = None) -> int:
+                  round_begin: int = 0, round_end: int | None = None, doc_start=None) -> int:
     """Brute-force count of allowed (query, key) score entries for one (batch, head) of
     rank ``rank``'s share, where each owner holds ``rows`` rows (Nq = n = rows)."""
     blocks = ring_blocks(c, rank, round_begin, round_end)
@@ -217,7 +240,9 @@ def allowed_count(c: int, rank: int, rows: int, causal: bool, zigzag: bool,
     pq = chunk_positions(rank, rows, c, zigzag)
     total = 0
     for j in blocks:
-        total += int(causal_allowed(pq, chunk_positions(j, rows, c, zigzag)).sum())
+        pk = chunk_positions(j, rows, c, zigzag)
+        m = causal_allowed(pq, pk) if doc_start is None else document_allowed(pq, pk, doc_start)
+        total += int(m.sum())
     return total
 
 

@@ -63,3 +63,17 @@ def test_unpinned_mutation_control():
     pins.test_t5_torch_sdpa_fp64(4, 2)
     pins.test_t4_share_rows_equal_full_sequence_rows(True)
     assert np.isfinite(A.score_scale(64))
+
+
+def test_document_start_off_by_one_is_caught(monkeypatch):
+    def bad(pq, pk, ds):
+        lo = np.asarray(ds, dtype=np.int64)[pq]
+        return (pk[None, :] <= pq[:, None]) & (pk[None, :] > lo[:, None])   # drops the first token
+    monkeypatch.setattr(A, "document_allowed", bad)
+    _expect_pin_failure(pins.test_t8_documents_equal_separate_causal_attention, [10, 1, 1, 20, 32])
+
+
+def test_document_mask_ignored_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "document_allowed", lambda pq, pk, ds: A.causal_allowed(pq, pk))
+    _expect_pin_failure(pins.test_t8_documents_equal_separate_causal_attention, [17, 15, 16, 16])
+    _expect_pin_failure(pins.test_t8_documents_bruteforce_50_digits, True)

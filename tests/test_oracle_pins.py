@@ -267,3 +267,113 @@ def test_sampled_rows_match_full():
     # same arithmetic on a different row grouping: equal up to BLAS rounding
     np.testing.assert_allclose(o, out[rows[:, 0], rows[:, 1], rows[:, 2]], rtol=0, atol=1e-14)
     np.testing.assert_allclose(l, lse[rows[:, 0], rows[:, 1], rows[:, 2]], rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------------------- T8
+# Document mask of packed sequences ("Why did Llama 3 not use a ring?"): the query at p
+# sees the keys of its own document up to itself.
+def _docs(S, lengths):
+    from blockwise_ring_attention_amd.inputs import doc_start_from_lengths
+    assert sum(lengths) == S
+    return doc_start_from_lengths(lengths)
+
+
+DOC_LAYOUTS = [[64], [1, 63], [10, 1, 1, 20, 32], [17, 15, 16, 16], [5] * 12 + [4]]
+
+
+@pytest.mark.parametrize("lengths", DOC_LAYOUTS)
+def test_t8_documents_equal_separate_causal_attention(lengths):
+    """Each document attends like an independent causal sequence: torch's fp64 causal
+    attention on every document span separately equals the oracle's rows (c = 1)."""
+    import torch
+    import torch.nn.functional as F
+    S, d, hq, hkv = 64, 8, 4, 2
+    qg, kg, vg = _global(2, hq, hkv, S, d, seed=81)
+    ds = _docs(S, lengths)
+    out, lse = oracle.rank_forward(qg, kg[None], vg[None], 1, 0, True, False, doc_start=ds)
+    a = 0
+    for n in lengths:
+        sl = slice(a, a + n)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(qg[:, :, sl]), torch.from_numpy(kg[:, :, sl]),
+                                             torch.from_numpy(vg[:, :, sl]), is_causal=True, enable_gqa=True).numpy()
+        np.testing.assert_allclose(out[:, :, sl], ref, rtol=0, atol=1e-13)
+        a += n
+
+
+def _mp_doc_bruteforce(qg, kg, vg, ds):
+    import mpmath as mp
+    mp.mp.dps = 50
+    B, hq, S, d = qg.shape
+    kx, vx = expand_gqa(kg, hq), expand_gqa(vg, hq)
+    inv = 1 / mp.sqrt(d)
+    out = np.zeros(qg.shape)
+    lse = np.zeros(qg.shape[:3])
+    for b in range(B):
+        for h in range(hq):
+            for p in range(S):
+                keys = range(int(ds[p]), p + 1)
+                w = [mp.exp(mp.fsum(mp.mpf(float(qg[b, h, p, i])) * mp.mpf(float(kx[b, h, u, i]))
+                                    for i in range(d)) * inv) for u in keys]
+                z = mp.fsum(w)
+                lse[b, h, p] = float(mp.log(z))
+                for e in range(d):
+                    out[b, h, p, e] = float(mp.fsum(wu * mp.mpf(float(vx[b, h, u, e]))
+                                                    for wu, u in zip(w, keys)) / z)
+    return out, lse
+
+
+@pytest.mark.parametrize("zigzag", [False, True])
+def test_t8_documents_bruteforce_50_digits(zigzag):
+    S, d, hq, hkv, c = 16, 4, 2, 1, 2
+    qg, kg, vg = _global(1, hq, hkv, S, d, seed=83)
+    ds = _docs(S, [3, 1, 7, 5])
+    ref_out, ref_lse = _mp_doc_bruteforce(qg, kg, vg, ds)
+    for rank in range(c):
+        q, kb, vb, own = build_share(qg, kg, vg, c, rank, zigzag)
+        out, lse = oracle.rank_forward(q, kb, vb, c, rank, True, zigzag, doc_start=ds)
+        np.testing.assert_allclose(out, ref_out[:, :, own[rank]], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, ref_lse[:, :, own[rank]], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("zigzag", [False, True])
+def test_t8_one_document_is_the_causal_mask(zigzag):
+    c, S, d, hq, hkv = 4, 64, 8, 4, 2
+    qg, kg, vg = _global(1, hq, hkv, S, d, seed=85)
+    for rank in range(c):
+        q, kb, vb, _ = build_share(qg, kg, vg, c, rank, zigzag)
+        a = oracle.rank_forward(q, kb, vb, c, rank, True, zigzag)
+        b = oracle.rank_forward(q, kb, vb, c, rank, True, zigzag, doc_start=np.zeros(S, dtype=np.int32))
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("zigzag", [False, True])
+def test_t8_document_shares_and_closed_form(zigzag):
+    """Shares gathered out of the full sequence, and Q = 0: uniform weights over the
+    document prefix, so lse = ln(p - start + 1) and out = the mean of those V rows."""
+    c, S, d, hq, hkv = 4, 64, 8, 4, 2
+    qg, kg, vg = _global(1, hq, hkv, S, d, seed=87)
+    ds = _docs(S, [9, 23, 1, 2, 29])
+    full, _ = oracle.rank_forward(qg, kg[None], vg[None], 1, 0, True, False, doc_start=ds)
+    vx = expand_gqa(vg, hq)
+    for rank in range(c):
+        q, kb, vb, own = build_share(qg, kg, vg, c, rank, zigzag)
+        out, _ = oracle.rank_forward(q, kb, vb, c, rank, True, zigzag, doc_start=ds)
+        np.testing.assert_allclose(out, full[:, :, own[rank]], rtol=0, atol=1e-13)
+        q0, _, _, _ = build_share(np.zeros_like(qg), kg, vg, c, rank, zigzag)
+        out0, lse0 = oracle.rank_forward(q0, kb, vb, c, rank, True, zigzag, doc_start=ds)
+        pos = own[rank]
+        np.testing.assert_allclose(lse0[0], np.broadcast_to(np.log(pos - ds[pos] + 1.0), lse0[0].shape),
+                                   rtol=0, atol=1e-13)
+        for i, p in enumerate(pos):
+            np.testing.assert_allclose(out0[0, :, i], vx[0, :, ds[p]:p + 1].mean(axis=1), rtol=0, atol=1e-13)
+
+
+def test_t8_document_allowed_counts():
+    """The brute-force allowed count with documents is sum over rows of p - start + 1."""
+    c, rows = 4, 16
+    S = c * rows
+    ds = _docs(S, [9, 23, 1, 2, 29])
+    for zigzag in (False, True):
+        total = sum(oracle.allowed_count(c, r, rows, True, zigzag, doc_start=ds) for r in range(c))
+        assert total == int(np.sum(np.arange(S) - ds + 1))
