@@ -49,12 +49,20 @@ def measured_traffic(workload: str, launch_ms: float):
 
 def workload_numbers(w):
     from blockwise_ring_attention_amd import accounting as acc
+    from blockwise_ring_attention_amd.inputs import make_doc_start
     n = w.rows
-    entries = acc.allowed_entries(w.c, w.rank, n, n, w.causal, w.zigzag)
-    flop = acc.unmasked_flop(w.batch, w.hq, w.head_dim, entries)
     eb = 2 if w.dtype == "bf16" else 4
-    nbytes = acc.algorithmic_bytes(w.batch, w.hq, w.hkv, n, n, w.head_dim, eb, w.c, w.rank, w.causal, w.zigzag,
-                                   with_lse=w.with_lse)
+    ds = make_doc_start(w)
+    if ds is not None:
+        entries = acc.doc_allowed_entries(w.c, w.rank, n, w.zigzag, ds)
+        kv_rows = acc.doc_needed_kv_rows(w.c, w.rank, n, w.zigzag, ds)
+        io = 2 * w.batch * w.hq * n * w.head_dim * eb + (4 * w.batch * w.hq * n if w.with_lse else 0)
+        nbytes = io + 2 * w.batch * w.hkv * kv_rows * w.head_dim * eb
+    else:
+        entries = acc.allowed_entries(w.c, w.rank, n, n, w.causal, w.zigzag)
+        nbytes = acc.algorithmic_bytes(w.batch, w.hq, w.hkv, n, n, w.head_dim, eb, w.c, w.rank, w.causal, w.zigzag,
+                                       with_lse=w.with_lse)
+    flop = acc.unmasked_flop(w.batch, w.hq, w.head_dim, entries)
     return flop, nbytes
 
 
@@ -62,11 +70,12 @@ def time_workload(w, steps: int, warmup: int, arrays=None):
     import torch
     import blockwise_ring_attention_amd as ra
     qd, kd, vd = _device_inputs(w, arrays)
+    fwd = _forward_fn(w)
     out = torch.empty_like(qd)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda") if w.with_lse else None
 
     def step():
-        ra.rank_forward(qd, kd, vd, w.c, w.rank, w.causal, w.zigzag, out=out, lse=lse, with_lse=w.with_lse)
+        fwd(qd, kd, vd, out=out, lse=lse, with_lse=w.with_lse)
 
     for _ in range(warmup):
         step()
@@ -97,6 +106,20 @@ def _device_inputs(w, arrays):
             torch.from_numpy(v).to("cuda", dt))
 
 
+def _forward_fn(w):
+    """ra.rank_forward for the workload, or ra.rank_forward_doc with its document layout
+    (uploaded once) when it has one; same call signature either way."""
+    import torch
+    import blockwise_ring_attention_amd as ra
+    from blockwise_ring_attention_amd.inputs import make_doc_start
+    ds = make_doc_start(w)
+    if ds is None:
+        return lambda q, k, v, t0=0, t1=None, **kw: ra.rank_forward(q, k, v, w.c, w.rank, w.causal, w.zigzag,
+                                                                    t0, t1, **kw)
+    dd = torch.from_numpy(ds).to("cuda")
+    return lambda q, k, v, t0=0, t1=None, **kw: ra.rank_forward_doc(q, k, v, dd, w.c, w.rank, w.zigzag, t0, t1, **kw)
+
+
 def time_per_round(w, steps: int, warmup: int, arrays=None):
     """The streamed form of the same share, as a live ring rank runs it: one launch per
     ring round (rounds [t, t+1)), each partial merged with ra_merge into the running
@@ -106,6 +129,7 @@ def time_per_round(w, steps: int, warmup: int, arrays=None):
     import torch
     import blockwise_ring_attention_amd as ra
     qd, kd, vd = _device_inputs(w, arrays)
+    fwd = _forward_fn(w)
     acc = torch.empty_like(qd)
     acc_lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
     part = torch.empty_like(qd)
@@ -114,9 +138,9 @@ def time_per_round(w, steps: int, warmup: int, arrays=None):
 
     def launch(t):
         if t == 0:
-            ra.rank_forward(qd, kd, vd, c, w.rank, w.causal, w.zigzag, 0, 1, out=acc, lse=acc_lse)
+            fwd(qd, kd, vd, 0, 1, out=acc, lse=acc_lse)
         else:
-            ra.rank_forward(qd, kd, vd, c, w.rank, w.causal, w.zigzag, t, t + 1, out=part, lse=part_lse)
+            fwd(qd, kd, vd, t, t + 1, out=part, lse=part_lse)
 
     def merge():
         ra.merge(acc, acc_lse, part, part_lse, out=acc, lse=acc_lse)
@@ -151,7 +175,7 @@ def time_per_round(w, steps: int, warmup: int, arrays=None):
     torch.cuda.synchronize()
     round_ms = [ev[t][0].elapsed_time(ev[t][1]) for t in range(c)]
     merge_ms = [ev[t][2].elapsed_time(ev[t][3]) for t in range(1, c)]
-    fused, fused_lse = ra.rank_forward(qd, kd, vd, c, w.rank, w.causal, w.zigzag, with_lse=True)
+    fused, fused_lse = fwd(qd, kd, vd, with_lse=True)
     torch.cuda.synchronize()
     diff = (acc.float() - fused.float()).abs().max().item()
     fin = torch.isfinite(fused_lse)
@@ -197,8 +221,10 @@ def cpu_baseline(w, arrays, min_seconds: float = 10.0):
     at least `min_seconds` (or covers the whole share); that run is reported."""
     import numpy as np
     import oracle
+    from blockwise_ring_attention_amd.inputs import make_doc_start
     q, k, v = arrays
     n = w.rows
+    ds = make_doc_start(w)
     total_rows = w.hq * n
     count = 96
     while True:
@@ -206,14 +232,17 @@ def cpu_baseline(w, arrays, min_seconds: float = 10.0):
         idx = np.arange(count)
         rows = np.stack([np.zeros_like(idx), idx // n, idx % n], axis=1)
         t0 = time.perf_counter()
-        oracle.rank_forward(q, k, v, w.c, w.rank, w.causal, w.zigzag, rows=rows)
+        oracle.rank_forward(q, k, v, w.c, w.rank, w.causal, w.zigzag, rows=rows, doc_start=ds)
         sec = time.perf_counter() - t0
         if sec >= min_seconds or count == total_rows:
             break
         count *= 2
     # unmasked work of the sampled rows: allowed keys per row
     ts = rows[:, 2]
-    if w.causal:
+    if ds is not None:
+        p = oracle.chunk_positions(w.rank, n, w.c, w.zigzag)[ts]
+        allowed = int(np.clip(p - np.maximum(ds[p], 0) + 1, 0, None).sum())
+    elif w.causal:
         allowed = int((oracle.chunk_positions(w.rank, n, w.c, w.zigzag)[ts] + 1).sum())
     else:
         allowed = len(ts) * n * w.c

@@ -14,7 +14,7 @@ from __future__ import annotations
 from . import _binding
 from ._binding import RaError, RaValueError, last_error, version  # noqa: F401
 
-__all__ = ["rank_forward", "merge", "version", "last_error", "RaError", "RaValueError"]
+__all__ = ["rank_forward", "rank_forward_doc", "merge", "version", "last_error", "RaError", "RaValueError"]
 
 
 def _dtype_code(t):
@@ -46,6 +46,28 @@ def rank_forward(q, k_blocks, v_blocks, c: int, rank: int, causal: bool, zigzag:
     Returns (out [B, Hq, Nq, d] in q's dtype, lse [B, Hq, Nq] fp32 or None).
     ``out``/``lse`` may be preallocated; the call is asynchronous on the current stream.
     """
+    return _forward(q, k_blocks, v_blocks, None, c, rank, causal, zigzag, round_begin, round_end, out, lse, with_lse)
+
+
+def rank_forward_doc(q, k_blocks, v_blocks, doc_start, c: int, rank: int, zigzag: bool,
+                     round_begin: int = 0, round_end: int | None = None, *, out=None, lse=None,
+                     with_lse: bool = True):
+    """``rank_forward`` (causal) with the document mask of a packed sequence: the query
+    at global position p sees the keys at positions doc_start[p] <= x <= p.
+
+    doc_start [c * n] int32 on the GPU: for each global position, where its document
+    begins. Other arguments and the result are those of ``rank_forward``.
+    """
+    import torch
+    if not doc_start.is_cuda or doc_start.dtype != torch.int32 or not doc_start.is_contiguous():
+        raise ValueError("doc_start must be a contiguous int32 GPU tensor")
+    if doc_start.dim() != 1 or doc_start.numel() != c * k_blocks.shape[3]:
+        raise ValueError(f"doc_start needs c * n = {c * k_blocks.shape[3]} entries, got {tuple(doc_start.shape)}")
+    return _forward(q, k_blocks, v_blocks, doc_start, c, rank, True, zigzag, round_begin, round_end, out, lse,
+                    with_lse)
+
+
+def _forward(q, k_blocks, v_blocks, doc_start, c, rank, causal, zigzag, round_begin, round_end, out, lse, with_lse):
     import torch
     if round_end is None:
         round_end = c
@@ -71,10 +93,16 @@ def rank_forward(q, k_blocks, v_blocks, c: int, rank: int, causal: bool, zigzag:
         lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
     elif lse is not None and (lse.shape != (B, hq, nq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, Nq]")
-    code = _binding.ra_rank_forward(_ptr(q), _ptr(k_blocks), _ptr(v_blocks), _ptr(out), _ptr(lse),
-                                    B, hq, hkv, nq, nkv, d, c, rank, causal, zigzag, round_begin, round_end, dt,
-                                    _stream_handle(q.device))
-    _binding.check(code, "ra_rank_forward")
+    if doc_start is None:
+        code = _binding.ra_rank_forward(_ptr(q), _ptr(k_blocks), _ptr(v_blocks), _ptr(out), _ptr(lse),
+                                        B, hq, hkv, nq, nkv, d, c, rank, causal, zigzag, round_begin, round_end, dt,
+                                        _stream_handle(q.device))
+        _binding.check(code, "ra_rank_forward")
+    else:
+        code = _binding.ra_rank_forward_doc(_ptr(q), _ptr(k_blocks), _ptr(v_blocks), _ptr(doc_start), _ptr(out),
+                                            _ptr(lse), B, hq, hkv, nq, nkv, d, c, rank, zigzag, round_begin,
+                                            round_end, dt, _stream_handle(q.device))
+        _binding.check(code, "ra_rank_forward_doc")
     return out, lse
 
 

@@ -15,6 +15,8 @@ n contiguous), derived from the zigzag pairing of "What breaks the load balance?
 
 from __future__ import annotations
 
+import numpy as np
+
 
 def block_allowed(c: int, rank: int, j: int, nq: int, n: int, causal: bool, zigzag: bool) -> int:
     """Allowed score entries of one (batch, query head) against KV block ``j``."""
@@ -82,3 +84,35 @@ def ring_break_even_tokens(flops_per_s: float, bytes_per_s: float) -> float:
     lasts as long as sending the next block (4 c d bytes): c >= F / B ("When is the
     ring actually free?"). The head dimension cancels."""
     return flops_per_s / bytes_per_s
+
+
+def share_positions(c: int, rank: int, rows: int, zigzag: bool) -> np.ndarray:
+    """Global positions of a rank's ``rows`` query rows: chunk ``rank`` of c, or (zigzag)
+    chunks ``rank`` and 2c-1-rank of 2c, in row order."""
+    if not zigzag:
+        return rank * rows + np.arange(rows, dtype=np.int64)
+    m = rows // 2
+    return np.concatenate([rank * m + np.arange(m, dtype=np.int64),
+                           (2 * c - 1 - rank) * m + np.arange(m, dtype=np.int64)])
+
+
+def doc_allowed_entries(c: int, rank: int, rows: int, zigzag: bool, doc_start) -> int:
+    """Allowed entries of one (batch, query head) over the whole ring under the document
+    mask: the query at p sees the keys at doc_start[p] .. p, so it counts p - start + 1
+    (none when the start lies past p)."""
+    pos = share_positions(c, rank, rows, zigzag)
+    lo = np.maximum(np.asarray(doc_start, dtype=np.int64)[pos], 0)
+    return int(np.clip(pos - lo + 1, 0, None).sum())
+
+
+def doc_needed_kv_rows(c: int, rank: int, rows: int, zigzag: bool, doc_start) -> int:
+    """Key positions some query of the share may see under the document mask: the size
+    of the union of the intervals [doc_start[p], p]."""
+    S = c * rows
+    pos = share_positions(c, rank, rows, zigzag)
+    lo = np.maximum(np.asarray(doc_start, dtype=np.int64)[pos], 0)
+    keep = lo <= pos
+    cover = np.zeros(S + 1, dtype=np.int64)
+    np.add.at(cover, lo[keep], 1)
+    np.add.at(cover, pos[keep] + 1, -1)
+    return int((np.cumsum(cover[:S]) > 0).sum())

@@ -99,13 +99,22 @@ __device__ inline int query_pos(const FwdArgs& a, int t) {
 // (rank - t) mod c; a block is one segment (contiguous/non-causal) or two (zigzag:
 // its early chunk in rows [0, m), its late chunk in rows [m, 2m)). Causal: only the
 // rows a query of the tile may see are visited, so fully masked tiles are skipped.
+// What a query tile's cursor needs about its queries: the positions of its first and
+// last row (causal) and, under the document mask, the smallest and largest first visible
+// position of its rows (0 without the mask, which changes nothing).
+struct QRange {
+  int lo, hi;       // positions of the tile's first and last query row
+  int dmin, dmax;   // min / max over the tile's rows of the document start
+};
+
 template <int BN>
 struct KvCursor {
   int t, seg, r, rend, slim, pdelta, blk;
-  int mrow;    // a 32-key run starting at segment row x may hold masked entries iff x > mrow
+  int mrow;    // a 32-key run starting at segment row x may hold masked entries if x > mrow
+  int mlow;    // ... or if x < mlow (keys before some row's document start)
   int valid;   // int, not bool: keeps the struct a plain array of words that SROA splits
 
-  __device__ inline bool enter(const FwdArgs& a, int qlo, int qhi) {
+  __device__ inline bool enter(const FwdArgs& a, const QRange& q) {
     blk = a.rank - t;
     if (blk < 0) blk += a.c;
     int r0;
@@ -121,38 +130,69 @@ struct KvCursor {
     }
     rend = slim;
     // A run [x, x+32) needs a mask when it passes the segment's end, or (causal) when its
-    // last key lies after the tile's first query.
+    // last key lies after the tile's first query, or when it starts before the document
+    // start of some row. Rows before every row's document start are not visited.
     mrow = slim - 32;
+    mlow = -1;
     if (a.causal) {
-      const int lim = qhi - pdelta + 1;   // rows whose position <= qhi
+      const int lim = q.hi - pdelta + 1;   // rows whose position <= the last query's
       rend = max(r0, min(rend, lim));
-      mrow = min(mrow, qlo - pdelta - 31);
+      mrow = min(mrow, q.lo - pdelta - 31);
+      mlow = q.dmax - pdelta;
+      r0 = max(r0, q.dmin - pdelta);
     }
     r = r0;
     return r < rend;
   }
-  __device__ inline void seek(const FwdArgs& a, int qlo, int qhi) {
+  __device__ inline void seek(const FwdArgs& a, const QRange& q) {
     const int nseg = (a.causal && a.zigzag) ? 2 : 1;
     while (t < a.t1) {
-      if (enter(a, qlo, qhi)) { valid = 1; return; }
+      if (enter(a, q)) { valid = 1; return; }
       if (++seg == nseg) { seg = 0; ++t; }
     }
     valid = 0;
   }
-  __device__ inline void begin(const FwdArgs& a, int qlo, int qhi) {
-    t = a.t0; seg = 0; seek(a, qlo, qhi);
+  __device__ inline void begin(const FwdArgs& a, const QRange& q) {
+    t = a.t0; seg = 0; seek(a, q);
   }
-  __device__ inline void next(const FwdArgs& a, int qlo, int qhi) {
+  __device__ inline void next(const FwdArgs& a, const QRange& q) {
     r += BN;
     if (r < rend) return;
     const int nseg = (a.causal && a.zigzag) ? 2 : 1;
     if (++seg == nseg) { seg = 0; ++t; }
-    seek(a, qlo, qhi);
+    seek(a, q);
   }
-  __device__ inline bool key_ok(const FwdArgs& a, int row, int qpos) const {
-    return row < slim && (!a.causal || pdelta + row <= qpos);
+  // The key at segment row `row` is visible to the query at qpos whose document starts at
+  // qds (0 without the document mask). Non-short-circuit operators: callers apply it as a
+  // select (see mask_sub).
+  __device__ inline bool key_ok(const FwdArgs& a, int row, int qpos, int qds) const {
+    const int pos = pdelta + row;
+    return (row < slim) & ((a.causal == 0) | ((pos <= qpos) & (pos >= qds)));
   }
 };
+
+// The tile's QRange: positions qlo..qhi are contiguous (a tile never straddles a zigzag
+// chunk). Under the document mask every wave reduces doc_start over those positions
+// (at most 4 loads per lane, once per workgroup); the reduction is wave-uniform.
+__device__ inline QRange tile_range(const FwdArgs& a, int qlo, int qhi, int lane) {
+  QRange q{qlo, qhi, 0, 0};
+  if (a.doc != nullptr) {
+    int mn = 0x7fffffff, mx = -0x7fffffff - 1;
+    for (int p = qlo + lane; p <= qhi; p += 64) {
+      const int v = a.doc[p];
+      mn = min(mn, v);
+      mx = max(mx, v);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      mn = min(mn, __shfl_xor(mn, off));
+      mx = max(mx, __shfl_xor(mx, off));
+    }
+    q.dmin = __builtin_amdgcn_readfirstlane(mn);
+    q.dmax = __builtin_amdgcn_readfirstlane(mx);
+  }
+  return q;
+}
 
 // v_permlane32_swap on two copies of x: afterwards lo = [x(0..31), x(0..31)] and
 // hi = [x(32..63), x(32..63)], so lo op hi combines each lane with lane ^ 32. Issued as
@@ -314,15 +354,23 @@ struct SubInfo {
 
 __device__ inline SubInfo sub_info(const KvCursor<64>& c, int sub) {
   const int r = c.r + 32 * sub;
-  return SubInfo{r, c.slim, c.pdelta, r > c.mrow};
+  return SubInfo{r, c.slim, c.pdelta, r > c.mrow || r < c.mlow};
 }
 
-// Set masked scores of a sub-tile to -inf. Lane (col, hf) holds keys 8*(e/4) + 4*hf + e%4.
-__device__ inline void mask_sub(const FwdArgs& a, const SubInfo& si, int hf, int qpos, f32x16& s) {
+// Set masked scores of a sub-tile to -inf. Lane (col, hf) holds keys 8*(e/4) + 4*hf + e%4
+// of its query at qpos, whose document starts at qds. The predicate is combined with
+// non-short-circuit operators and applied as a select, so no lane-divergent branch
+// writes the score registers. (Written with short-circuit operators and an if, the
+// compiler's divergent-branch lowering of this loop dropped the masking store for some
+// lanes; see the document-mask parity tests.)
+__device__ inline void mask_sub(const FwdArgs& a, const SubInfo& si, int hf, int qpos, int qds, f32x16& s) {
+  const bool causal = a.causal != 0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int row = si.r + 8 * (e >> 2) + 4 * hf + (e & 3);
-    if (!(row < si.slim && (!a.causal || si.pdelta + row <= qpos))) s[e] = kNegInf;
+    const int pos = si.pdelta + row;
+    const bool ok = (row < si.slim) & (!causal | ((pos <= qpos) & (pos >= qds)));
+    s[e] = ok ? s[e] : kNegInf;
   }
 }
 
@@ -396,13 +444,13 @@ __device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const
 // rescales O (which already holds the P.V products issued in this step, taken against
 // the old reference) and the sum, and recomputes p. Masked scores are -inf and give 0.
 template <int D, bool QK, bool PV, bool SM>
-__device__ __forceinline__ void pipe_step(const FwdArgs& a, const SubInfo& si, int hf, int qlo, int qpos, float sc,
+__device__ __forceinline__ void pipe_step(const FwdArgs& a, const SubInfo& si, int hf, int qds, int qpos, float sc,
                                           const char* kt, const char* vt, const bf16x8 (&qf)[D / 16],
                                           const int (&koff)[D / 16], const int (&voff)[D / 32],
                                           const bf16x8 (&pp)[2], f32x16 (&o)[D / 32], f32x16& sn, f32x16& scur,
                                           bf16x8 (&pc)[2], float& mref, float& lsum) {
   constexpr int NDV = D / 32;
-  if (SM && si.mask) mask_sub(a, si, hf, qpos, scur);
+  if (SM && si.mask) mask_sub(a, si, hf, qpos, qds, scur);
   const float nm = -mref;
   f32x16 e;
   float ps;
@@ -465,6 +513,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int qpos = a.causal ? query_pos(a, min(row, tile.row_end - 1)) : 0;
   const int qlo = a.causal ? query_pos(a, tile.row0) : 0;
   const int qhi = a.causal ? query_pos(a, tile.row_end - 1) : 0;
+  const QRange qr = tile_range(a, qlo, qhi, lane);
+  const int qds = a.doc != nullptr ? a.doc[qpos] : 0;   // first key position the lane's query sees
 
   // Q^T fragments: lane (col, hf) holds dims 16*ks + 8*hf .. +7 of its query row.
   bf16x8 qf[NKS];
@@ -527,14 +577,14 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // unrolled over them, so the compiler can tell a stage's reads apart from the loads in
   // flight into the other buffers. Even sub-tiles use (sA, pA), odd ones (sB, pB).
   KvCursor<BN> lc, cc;   // next stage to load, stage being folded
-  lc.begin(a, qlo, qhi);
+  lc.begin(a, qr);
   cc = lc;
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < NB - 2; ++s) {
     if (lc.valid) {
       issue(kb[s], vb[s], lc);
-      lc.next(a, qlo, qhi);
+      lc.next(a, qr);
       ++issued;
     }
   }
@@ -547,15 +597,15 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     phase_barrier();
     if (lc.valid) {
       issue(kb[NB - 2], vb[NB - 2], lc);
-      lc.next(a, qlo, qhi);
+      lc.next(a, qr);
       ++issued;
     }
     SubInfo prev = sub_info(cc, 1);
-    pipe_step<D, true, false, false>(a, prev, hf, qlo, qpos, sc, kb[0], vb[0], qf, koff, voff, pB, o, sA, sB, pB,
+    pipe_step<D, true, false, false>(a, prev, hf, qds, qpos, sc, kb[0], vb[0], qf, koff, voff, pB, o, sA, sB, pB,
                                      mref, lsum);
-    pipe_step<D, true, false, true>(a, sub_info(cc, 0), hf, qlo, qpos, sc, kb[0] + 32 * L::ROWB, vb[0], qf, koff,
+    pipe_step<D, true, false, true>(a, sub_info(cc, 0), hf, qds, qpos, sc, kb[0] + 32 * L::ROWB, vb[0], qf, koff,
                                     voff, pB, o, sB, sA, pA, mref, lsum);
-    cc.next(a, qlo, qhi);
+    cc.next(a, qr);
     int s = 1;
     int last = 0;   // buffer of the last stage, for the tail
     if (cc.valid) {
@@ -568,17 +618,17 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
           phase_barrier();
           if (lc.valid) {
             issue(kb[(1 + u + NB - 2) % NB], vb[(1 + u + NB - 2) % NB], lc);
-            lc.next(a, qlo, qhi);
+            lc.next(a, qr);
             ++issued;
           }
           // step 2s-1: S of (s, sub 0); P.V of (s-1, sub 0); softmax of (s-1, sub 1)
-          pipe_step<D, true, true, true>(a, prev, hf, qlo, qpos, sc, kb[b], vb[bp], qf, koff, voff, pA, o, sA, sB, pB,
+          pipe_step<D, true, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf, koff, voff, pA, o, sA, sB, pB,
                                          mref, lsum);
           // step 2s: S of (s, sub 1); P.V of (s-1, sub 1); softmax of (s, sub 0)
-          pipe_step<D, true, true, true>(a, sub_info(cc, 0), hf, qlo, qpos, sc, kb[b] + 32 * L::ROWB,
+          pipe_step<D, true, true, true>(a, sub_info(cc, 0), hf, qds, qpos, sc, kb[b] + 32 * L::ROWB,
                                          vb[bp] + 32 * L::ROWB, qf, koff, voff, pB, o, sB, sA, pA, mref, lsum);
           prev = sub_info(cc, 1);
-          cc.next(a, qlo, qhi);
+          cc.next(a, qr);
           ++s;
           if (!cc.valid) {
             last = b;
@@ -592,9 +642,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (b == last) {
-        pipe_step<D, false, true, true>(a, prev, hf, qlo, qpos, sc, kb[b], vb[b], qf, koff, voff, pA, o, sA, sB, pB,
+        pipe_step<D, false, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[b], qf, koff, voff, pA, o, sA, sB, pB,
                                         mref, lsum);
-        pipe_step<D, false, true, false>(a, prev, hf, qlo, qpos, sc, kb[b], vb[b] + 32 * L::ROWB, qf, koff, voff, pB,
+        pipe_step<D, false, true, false>(a, prev, hf, qds, qpos, sc, kb[b], vb[b] + 32 * L::ROWB, qf, koff, voff, pB,
                                          o, sB, sA, pA, mref, lsum);
       }
     }
@@ -646,6 +696,8 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   const int qpos = a.causal ? query_pos(a, min(row, tile.row_end - 1)) : 0;
   const int qlo = a.causal ? query_pos(a, tile.row0) : 0;
   const int qhi = a.causal ? query_pos(a, tile.row_end - 1) : 0;
+  const QRange qr = tile_range(a, qlo, qhi, lane);
+  const int qds = a.doc != nullptr ? a.doc[qpos] : 0;
 
   float qf[DP / 2];
   const float* qrow = qg + (((size_t)tile.b * a.hq + head) * a.nq + (rvalid ? row : 0)) * d;
@@ -661,7 +713,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   const size_t head_off = ((size_t)tile.b * a.hkv + tile.g) * a.nkv * d;
 
   KvCursor<BN> cur;
-  cur.begin(a, qlo, qhi);
+  cur.begin(a, qr);
   while (cur.valid) {
     __syncthreads();
     const float* kb = kg + cur.blk * blk_stride + head_off;
@@ -678,11 +730,11 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < DP / 2; ++ks)
       if (2 * ks < d) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kl[col * KSF + 2 * ks + hf], qf[ks], s, 0, 0, 0);
-    if (cur.r > cur.mrow) {
+    if (cur.r > cur.mrow || cur.r < cur.mlow) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int krow = cur.r + 8 * (e >> 2) + 4 * hf + (e & 3);
-        if (!cur.key_ok(a, krow, qpos)) s[e] = kNegInf;
+        s[e] = cur.key_ok(a, krow, qpos, qds) ? s[e] : kNegInf;
       }
     }
     float mx = s[0];
@@ -712,7 +764,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
           o[dv] = __builtin_amdgcn_mfma_f32_32x32x2f32(vl[(8 * (e >> 2) + 4 * hf + (e & 3)) * VSF + 32 * dv + col],
                                                        s[e], o[dv], 0, 0, 0);
       }
-    cur.next(a, qlo, qhi);
+    cur.next(a, qr);
   }
 
   const float lt = xhalf_sum(lsum);

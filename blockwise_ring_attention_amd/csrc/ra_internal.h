@@ -12,6 +12,7 @@ struct FwdArgs {
   const void* v;
   void* out;
   float* lse;           // may be null
+  const int* doc;       // document starts by global position (causal document mask), or null
   int B, hq, hkv, nq, nkv, d;
   int c, rank, causal, zigzag, t0, t1;
   // Work decomposition (see plan_forward in ra_host.cpp).

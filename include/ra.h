@@ -96,6 +96,32 @@ int ra_rank_forward(const void* q, const void* k_blocks, const void* v_blocks,
                     int dtype, void* stream);
 
 /*
+ * ra_rank_forward_doc -- ra_rank_forward (always causal) with the document mask of a
+ * packed sequence: attention does not cross document boundaries, the mask Llama 3's
+ * all-gather context parallelism was chosen to support ("What do you do about long
+ * sequences and sparse models?", section "Why did Llama 3 not use a ring?").
+ *
+ *   doc_start [c * nkv] int32, device: for every global token position p, the position
+ *             where p's document begins (documents are contiguous spans, so the value
+ *             also identifies the document). The query at position p sees exactly
+ *             the keys at positions x with doc_start[p] <= x <= p. Any int32 values
+ *             are accepted with that meaning (a value above p leaves the row without
+ *             keys: out = 0, lse = -inf). Positions are those of ra_rank_forward
+ *             (zigzag or contiguous ownership of the sequence of c * nkv tokens).
+ *             Read-only; 4-byte aligned; must not be NULL unless batch or nq is 0.
+ *
+ * Every other argument, the layouts, outputs and errors are those of ra_rank_forward
+ * with causal = 1. Tiles of keys that lie before every document start of a query
+ * tile, or after its last query, are never loaded or computed.
+ */
+int ra_rank_forward_doc(const void* q, const void* k_blocks, const void* v_blocks,
+                        const int* doc_start, void* out, float* lse,
+                        int batch, int hq, int hkv, int nq, int nkv, int head_dim,
+                        int c, int rank, int zigzag,
+                        int round_begin, int round_end,
+                        int dtype, void* stream);
+
+/*
  * ra_merge -- combine two partial results over disjoint key sets into the result over
  * their union ("What do you do about long sequences and sparse models?", section "How
  * does attention survive being split?": partials combine exactly through their

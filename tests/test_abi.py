@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol(ra_lib):
 
 
 def test_version(ra_lib):
-    assert B.version() == 100
+    assert B.version() == 200
 
 
 FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced (every call below fails its checks)
@@ -62,6 +62,7 @@ def _fwd(**kw):
     (dict(nkv=32), B.RA_ERR_SHAPE),
     (dict(nq=63, nkv=63), B.RA_ERR_SHAPE),
     (dict(c=1 << 16, rank=0, t1=1, nq=1 << 15, nkv=1 << 15), B.RA_ERR_SHAPE),
+    (dict(c=1, rank=0, t1=1, nq=1 << 24, nkv=1 << 24), B.RA_ERR_SHAPE),   # 4 GiB K slab per head
     (dict(q=0), B.RA_ERR_ARG),
     (dict(out=0), B.RA_ERR_ARG),
     (dict(k=0), B.RA_ERR_ARG),
@@ -72,6 +73,34 @@ def _fwd(**kw):
 def test_forward_argument_errors(ra_lib, kw, code):
     assert _fwd(**kw) == code
     assert B.last_error() != ""
+
+
+def _fwd_doc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, doc=FAKE, out=FAKE, lse=FAKE, batch=1, hq=4, hkv=2, nq=64, nkv=64, d=128, c=4,
+             rank=1, zigzag=1, t0=0, t1=4, dtype=B.RA_BF16)
+    a.update(kw)
+    return B.ra_rank_forward_doc(a["q"], a["k"], a["v"], a["doc"], a["out"], a["lse"], a["batch"], a["hq"], a["hkv"],
+                                 a["nq"], a["nkv"], a["d"], a["c"], a["rank"], a["zigzag"], a["t0"], a["t1"],
+                                 a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(doc=0), B.RA_ERR_ARG),
+    (dict(doc=FAKE + 2), B.RA_ERR_ALIGN),
+    (dict(rank=4), B.RA_ERR_ARG),
+    (dict(nkv=32), B.RA_ERR_SHAPE),          # always causal: nq == nkv
+    (dict(nq=63, nkv=63), B.RA_ERR_SHAPE),   # zigzag needs an even nkv
+    (dict(d=96), B.RA_ERR_UNSUPPORTED),
+    (dict(q=FAKE + 8), B.RA_ERR_ALIGN),
+])
+def test_forward_doc_argument_errors(ra_lib, kw, code):
+    assert _fwd_doc(**kw) == code
+    assert B.last_error() != ""
+
+
+def test_forward_doc_empty_is_a_noop(ra_lib):
+    assert _fwd_doc(batch=0, q=0, k=0, v=0, doc=0, out=0, lse=0) == B.RA_OK
+    assert _fwd_doc(nq=0, nkv=0, q=0, k=0, v=0, doc=0, out=0, lse=0) == B.RA_OK
 
 
 def test_forward_empty_is_a_noop(ra_lib):

@@ -89,3 +89,39 @@ def test_workload_flops_and_bytes():
     w3 = WORKLOADS["gqa32x8_d128_s32k_c8_zigzag_bf16"]
     e3 = acc.allowed_entries(w3.c, w3.rank, w3.rows, w3.rows, True, True)
     assert e3 == 67_110_912
+
+
+def test_document_counts_match_brute_force():
+    """The closed-form document-mask counts used by the bench equal the oracle's
+    brute-force counts (allowed entries) and a direct union of visible key positions."""
+    import numpy as np
+    import oracle
+    from blockwise_ring_attention_amd import accounting as acc
+    from blockwise_ring_attention_amd.inputs import doc_start_from_lengths, draw_document_lengths
+    c, rows = 4, 32
+    S = c * rows
+    for seed, layout in enumerate([draw_document_lengths(S, 9, 1.0, 3), [S], [1] * S]):
+        ds = doc_start_from_lengths(layout)
+        for zigzag in (False, True):
+            for r in range(c):
+                assert acc.doc_allowed_entries(c, r, rows, zigzag, ds) == \
+                    oracle.allowed_count(c, r, rows, True, zigzag, doc_start=ds)
+                pos = oracle.chunk_positions(r, rows, c, zigzag)
+                seen = set()
+                for p in pos:
+                    seen.update(range(int(ds[p]), int(p) + 1))
+                assert acc.doc_needed_kv_rows(c, r, rows, zigzag, ds) == len(seen)
+    # a start past the query leaves the row empty
+    ds = np.arange(S, dtype=np.int32) + 1
+    assert acc.doc_allowed_entries(c, 1, rows, True, ds) == 0
+    assert acc.doc_needed_kv_rows(c, 1, rows, True, ds) == 0
+
+
+def test_binding_rejects_host_doc_start():
+    import pytest
+    import torch
+    import blockwise_ring_attention_amd as ra
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(2, 1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="doc_start"):
+        ra.rank_forward_doc(q, k, k, torch.zeros(8, dtype=torch.int32), 2, 0, True)

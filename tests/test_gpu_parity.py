@@ -177,3 +177,20 @@ def test_binding_rejects_bad_tensors():
     k2 = torch.zeros((2, 1, 2, 64, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         ra.rank_forward(torch.zeros((1, 4, 64, 96), dtype=torch.bfloat16, device="cuda"), k2, k2, 2, 0, True, True)
+
+
+def test_causal_mask_regression_inputs():
+    """Plain causal zigzag on the inputs that exposed a miscompiled mask: written with
+    short-circuit operators and an if, the compiler's lowering of the per-key mask lost
+    the masking store for some lanes whenever a query tile's diagonal fell in the first
+    32 keys of a stage (every query then saw up to 31 later keys)."""
+    B, hq, hkv, d, n, c, rank = 1, 8, 1, 128, 512, 4, 0
+    seed = 900 + n + c + rank
+    q = random_array((B, hq, n, d), "bf16", seed)
+    k = random_array((c, B, hkv, n, d), "bf16", seed + 1)
+    v = random_array((c, B, hkv, n, d), "bf16", seed + 2)
+    for zigzag in (True, False):
+        say(f"mask regression zigzag={zigzag}")
+        out, lse = run_gpu(q, k, v, c, rank, True, zigzag)
+        ref, ref_lse = oracle.rank_forward(q, k, v, c, rank, True, zigzag)
+        assert_parity(out, ref, lse, ref_lse, "bf16", "mask regression")
