@@ -192,19 +192,26 @@ def balance_sweep(w, steps: int, warmup: int):
     import dataclasses
     import torch
     from blockwise_ring_attention_amd import accounting as acc
-    from blockwise_ring_attention_amd.inputs import make_inputs
+    from blockwise_ring_attention_amd.inputs import make_doc_start, make_inputs
     arrays = make_inputs(w)
+    ds = make_doc_start(w)
     res = {}
     for zig in (False, True):
         ranks = []
         for r in range(w.c):
             wr = dataclasses.replace(w, rank=r, zigzag=zig)
             ms, ml, mn = time_workload(wr, steps, warmup, arrays)
-            e = acc.allowed_entries(w.c, r, w.rows, w.rows, True, zig)
+            if ds is None:
+                e = acc.allowed_entries(w.c, r, w.rows, w.rows, True, zig)
+            else:
+                e = acc.doc_allowed_entries(w.c, r, w.rows, zig, ds)
             flop = acc.unmasked_flop(w.batch, w.hq, w.head_dim, e)
-            units = sum(1 for j in range(w.c) if acc.block_allowed(w.c, r, j, w.rows, w.rows, True, zig) > 0)
-            ranks.append({"rank": r, "kernel_ms": round(ml, 4), "tflops": round(flop / (ml * 1e-3) / 1e12, 1),
-                          "allowed_entries_per_head": e, "kv_blocks_with_work": units})
+            rec = {"rank": r, "kernel_ms": round(ml, 4), "tflops": round(flop / (ml * 1e-3) / 1e12, 1),
+                   "allowed_entries_per_head": e}
+            if ds is None:
+                rec["kv_blocks_with_work"] = sum(
+                    1 for j in range(w.c) if acc.block_allowed(w.c, r, j, w.rows, w.rows, True, zig) > 0)
+            ranks.append(rec)
         times = [x["kernel_ms"] for x in ranks]
         res["zigzag" if zig else "contiguous"] = {
             "ranks": ranks, "max_ms": max(times), "min_ms": min(times),
