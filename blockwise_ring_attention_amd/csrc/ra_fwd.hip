@@ -281,7 +281,8 @@ struct StageLoader {
   }
 
   // kb, vb: row 0 of the slab (nkv rows of 2*D bytes; nkv * 2 * D < 2^31 is checked on
-  // the host).
+  // the host). DOK / DOV select the K and the V tile, so a stage's loads can be spread.
+  template <bool DOK = true, bool DOV = true>
   __device__ inline void issue(char* kst, char* vst, const __bf16* kb, const __bf16* vb, int r, int nkv) const {
     typedef __attribute__((address_space(3))) void lds_void;
     const int bytes = nkv * L::ROWB;
@@ -291,20 +292,24 @@ struct StageLoader {
     if (r + L::BN <= nkv) {
 #pragma unroll
       for (int u = 0; u < L::LOADS; ++u) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kst + (u * L::WAVES + wave) * 1024), 16, koff[u],
-                                                 soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vst + (u * L::WAVES + wave) * 1024), 16, voff[u],
-                                                 soff, 0, 0);
+        if (DOK)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kst + (u * L::WAVES + wave) * 1024), 16, koff[u],
+                                                   soff, 0, 0);
+        if (DOV)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vst + (u * L::WAVES + wave) * 1024), 16, voff[u],
+                                                   soff, 0, 0);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < L::LOADS; ++u) {
         // rows past the slab repeat its last row (masked out by the fold)
         const int back = max(0, r + row[u] - (nkv - 1)) * L::ROWB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kst + (u * L::WAVES + wave) * 1024), 16,
-                                                 soff + (int)koff[u] - back, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vst + (u * L::WAVES + wave) * 1024), 16,
-                                                 soff + (int)voff[u] - back, 0, 0, 0);
+        if (DOK)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kst + (u * L::WAVES + wave) * 1024), 16,
+                                                   soff + (int)koff[u] - back, 0, 0, 0);
+        if (DOV)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vst + (u * L::WAVES + wave) * 1024), 16,
+                                                   soff + (int)voff[u] - back, 0, 0, 0);
       }
     }
   }
@@ -560,12 +565,15 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   int slab_blk = -1;
   const __bf16* kslab = kg;
   const __bf16* vslab = vg;
-  auto issue = [&](char* kst, char* vst, const KvCursor<BN>& c) {
+  auto slab_for = [&](const KvCursor<BN>& c) {
     if (c.blk != slab_blk) {
       slab_blk = c.blk;
       kslab = kg + slab_blk * blk_stride + head_off;
       vslab = vg + slab_blk * blk_stride + head_off;
     }
+  };
+  auto issue = [&](char* kst, char* vst, const KvCursor<BN>& c) {
+    slab_for(c);
     ld.issue(kst, vst, kslab, vslab, c.r, a.nkv);
   };
 
@@ -573,7 +581,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // and 2s+1 and 2s+2 (its V). Each stage begins with a workgroup barrier, before which
   // every wave waits for its own loads of stage s: after it, stage s is complete in LDS
   // for everyone, and stage s - 2 (last read at step 2s - 2) is free, so the loads of
-  // stage s + NB - 2 go into its buffer. The buffers are distinct arrays and the loop is
+  // stage s + NB - 2 go into its buffer during stage s. The buffers are distinct arrays and the loop is
   // unrolled over them, so the compiler can tell a stage's reads apart from the loads in
   // flight into the other buffers. Even sub-tiles use (sA, pA), odd ones (sB, pB).
   KvCursor<BN> lc, cc;   // next stage to load, stage being folded
@@ -616,14 +624,24 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
           const int b = (1 + u) % NB, bp = u % NB;
           wait_stages<D>(issued - (s + 1));
           phase_barrier();
-          if (lc.valid) {
-            issue(kb[(1 + u + NB - 2) % NB], vb[(1 + u + NB - 2) % NB], lc);
-            lc.next(a, qr);
-            ++issued;
+          // The K tile of stage s + NB - 2 is issued before step 2s-1 and its V tile before
+          // step 2s: spreading a stage's loads over the stage beats issuing them in one burst.
+          const int bn = (1 + u + NB - 2) % NB;
+          const bool load = lc.valid;
+          const int load_row = lc.r;
+          if (load) {
+            slab_for(lc);
+            ld.template issue<true, false>(kb[bn], vb[bn], kslab, vslab, load_row, a.nkv);
           }
           // step 2s-1: S of (s, sub 0); P.V of (s-1, sub 0); softmax of (s-1, sub 1)
           pipe_step<D, true, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf, koff, voff, pA, o, sA, sB, pB,
                                          mref, lsum);
+          __builtin_amdgcn_sched_barrier(0);
+          if (load) {
+            ld.template issue<false, true>(kb[bn], vb[bn], kslab, vslab, load_row, a.nkv);
+            lc.next(a, qr);
+            ++issued;
+          }
           // step 2s: S of (s, sub 1); P.V of (s-1, sub 1); softmax of (s, sub 0)
           pipe_step<D, true, true, true>(a, sub_info(cc, 0), hf, qds, qpos, sc, kb[b] + 32 * L::ROWB,
                                          vb[bp] + 32 * L::ROWB, qf, koff, voff, pB, o, sB, sA, pA, mref, lsum);
