@@ -6,8 +6,9 @@
 One step = one fused launch of ra_rank_forward over the whole share (all c ring rounds,
 causal skipping, GQA, lse) on seeded synthetic inputs already resident in HBM. The value
 is unmasked TFLOP/s: 4*d FLOP per allowed score entry over the step time. Prints one
-JSON line; it also carries the streamed form of the same share (one launch per ring
-round merged with ra_merge, "per_round"). ``--balance`` instead times every rank of the
+JSON line; it also carries the streamed form of the same share ("per_round": one launch
+per ring round, folded into the running result by the kernel's own epilogue, and the same
+with a separate ra_merge launch per round). ``--balance`` instead times every rank of the
 workload with contiguous and with zigzag chunks and prints that sweep.
 """
 
@@ -120,35 +121,53 @@ def _forward_fn(w):
     return lambda q, k, v, t0=0, t1=None, **kw: ra.rank_forward_doc(q, k, v, dd, w.c, w.rank, w.zigzag, t0, t1, **kw)
 
 
-def time_per_round(w, steps: int, warmup: int, arrays=None):
+def _accumulate_fn(w):
+    """ra.rank_forward_accumulate for the workload (with its document layout if any)."""
+    import torch
+    import blockwise_ring_attention_amd as ra
+    from blockwise_ring_attention_amd.inputs import make_doc_start
+    ds = make_doc_start(w)
+    dd = torch.from_numpy(ds).to("cuda") if ds is not None else None
+    return lambda q, k, v, out, lse, t0, t1: ra.rank_forward_accumulate(q, k, v, out, lse, w.c, w.rank, w.causal,
+                                                                        w.zigzag, t0, t1, doc_start=dd)
+
+
+def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumulate"):
     """The streamed form of the same share, as a live ring rank runs it: one launch per
-    ring round (rounds [t, t+1)), each partial merged with ra_merge into the running
-    (out, lse) kept in HBM (in place, in the input dtype). One step = all c rounds.
-    Returns step ms, per-round kernel ms, per-merge ms (from one event-instrumented
-    step), and the max abs difference of the merged result from the fused launch."""
+    ring round (rounds [t, t+1)), in ring order. Round 0 writes the running (out, lse) in
+    HBM; each later round is folded into it, either inside the kernel's epilogue
+    (mode "accumulate": ra_rank_forward_accumulate) or by a separate in-place ra_merge of
+    that round's partial (mode "merge"). One step = all c rounds. Returns step ms,
+    per-round kernel ms, per-merge ms (from one event-instrumented step), and the max
+    abs difference of the streamed result from the fused launch."""
     import torch
     import blockwise_ring_attention_amd as ra
     qd, kd, vd = _device_inputs(w, arrays)
     fwd = _forward_fn(w)
+    accf = _accumulate_fn(w)
     acc = torch.empty_like(qd)
     acc_lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
-    part = torch.empty_like(qd)
-    part_lse = torch.empty_like(acc_lse)
+    part = torch.empty_like(qd) if mode == "merge" else None
+    part_lse = torch.empty_like(acc_lse) if mode == "merge" else None
     c = w.c
 
     def launch(t):
         if t == 0:
             fwd(qd, kd, vd, 0, 1, out=acc, lse=acc_lse)
-        else:
+        elif mode == "merge":
             fwd(qd, kd, vd, t, t + 1, out=part, lse=part_lse)
+        else:
+            accf(qd, kd, vd, acc, acc_lse, t, t + 1)
 
     def merge():
         ra.merge(acc, acc_lse, part, part_lse, out=acc, lse=acc_lse)
 
+    has_merge = mode == "merge"
+
     def step():
         for t in range(c):
             launch(t)
-            if t > 0:
+            if t > 0 and has_merge:
                 merge()
 
     for _ in range(warmup):
@@ -168,13 +187,13 @@ def time_per_round(w, steps: int, warmup: int, arrays=None):
         ev[t][0].record(stream)
         launch(t)
         ev[t][1].record(stream)
-        if t > 0:
+        if t > 0 and has_merge:
             ev[t][2].record(stream)
             merge()
             ev[t][3].record(stream)
     torch.cuda.synchronize()
     round_ms = [ev[t][0].elapsed_time(ev[t][1]) for t in range(c)]
-    merge_ms = [ev[t][2].elapsed_time(ev[t][3]) for t in range(1, c)]
+    merge_ms = [ev[t][2].elapsed_time(ev[t][3]) for t in range(1, c)] if has_merge else []
     fused, fused_lse = fwd(qd, kd, vd, with_lse=True)
     torch.cuda.synchronize()
     diff = (acc.float() - fused.float()).abs().max().item()
@@ -362,13 +381,19 @@ def main():
                          "pct_of_peak": round(100 * fa / (ms_a * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)})
         line["also"] = also
     if not args.no_per_round:
-        ms_pr, round_ms, merge_ms, diff, lse_diff = time_per_round(w, max(1, args.steps // 4), 1, arrays)
-        line["per_round"] = {
-            "what": "one launch per ring round (rounds [t, t+1)) + in-place ra_merge into the running (out, lse)",
-            "ms_per_step": round(ms_pr, 4), "value": round(flop / (ms_pr * 1e-3) / 1e12, 2),
-            "overhead_vs_fused": round(ms_pr / ms_step - 1.0, 4),
-            "round_kernel_ms": [round(x, 4) for x in round_ms], "merge_ms": [round(x, 4) for x in merge_ms],
-            "max_abs_diff_vs_fused": diff, "lse_max_abs_diff_vs_fused": lse_diff}
+        what = {"accumulate": "one ra_rank_forward_accumulate launch per ring round (rounds [t, t+1)), each "
+                              "folding its partial into the running (out, lse) in its epilogue",
+                "merge": "one ra_rank_forward launch per ring round + in-place ra_merge into the running "
+                         "(out, lse)"}
+        line["per_round"] = {}
+        for mode in ("accumulate", "merge"):
+            ms_pr, round_ms, merge_ms, diff, lse_diff = time_per_round(w, max(1, args.steps // 4), 1, arrays, mode)
+            line["per_round"][mode] = {
+                "what": what[mode],
+                "ms_per_step": round(ms_pr, 4), "value": round(flop / (ms_pr * 1e-3) / 1e12, 2),
+                "overhead_vs_fused": round(ms_pr / ms_step - 1.0, 4),
+                "round_kernel_ms": [round(x, 4) for x in round_ms], "merge_ms": [round(x, 4) for x in merge_ms],
+                "max_abs_diff_vs_fused": diff, "lse_max_abs_diff_vs_fused": lse_diff}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, arrays, args.cpu_seconds)
     torch.cuda.synchronize()

@@ -4,7 +4,8 @@
 the c key/value blocks of the ring, folded in ring order with the online softmax (the
 result equals full-row softmax attention), with the causal mask, zigzag chunk
 ownership, grouped-query heads and per-row logsumexp. ``merge`` combines two partial
-results over disjoint key sets. Both are thin wrappers over the C ABI of ``libra.so``
+results over disjoint key sets; ``rank_forward_accumulate`` folds some rounds straight into
+a running (out, lse), the streamed form of the ring. All are thin wrappers over the C ABI of ``libra.so``
 (``include/ra.h``): torch tensors supply device memory and the current stream; all
 arithmetic runs in the library's HIP kernels.
 """
@@ -14,7 +15,7 @@ from __future__ import annotations
 from . import _binding
 from ._binding import RaError, RaValueError, last_error, version  # noqa: F401
 
-__all__ = ["rank_forward", "rank_forward_doc", "merge", "version", "last_error", "RaError", "RaValueError"]
+__all__ = ["rank_forward", "rank_forward_doc", "rank_forward_accumulate", "merge", "version", "last_error", "RaError", "RaValueError"]
 
 
 def _dtype_code(t):
@@ -58,16 +59,42 @@ def rank_forward_doc(q, k_blocks, v_blocks, doc_start, c: int, rank: int, zigzag
     doc_start [c * n] int32 on the GPU: for each global position, where its document
     begins. Other arguments and the result are those of ``rank_forward``.
     """
+    _check_doc(doc_start, c, k_blocks)
+    return _forward(q, k_blocks, v_blocks, doc_start, c, rank, True, zigzag, round_begin, round_end, out, lse,
+                    with_lse)
+
+
+def rank_forward_accumulate(q, k_blocks, v_blocks, out, lse, c: int, rank: int, causal: bool, zigzag: bool,
+                            round_begin: int = 0, round_end: int | None = None, *, doc_start=None):
+    """Fold rounds [round_begin, round_end) into the running result (out, lse) in place.
+
+    ``out`` [B, Hq, Nq, d] (q's dtype) and ``lse`` [B, Hq, Nq] fp32 hold the result over
+    the keys folded so far (lse = -inf where none: start from ``lse.fill_(-inf)``; out
+    is then never read). Afterwards they hold the result over those keys and this call's
+    rounds, which must not repeat a round already folded in. ``doc_start`` (optional)
+    adds the document mask of ``rank_forward_doc`` (causal only). Returns (out, lse).
+    """
+    import torch
+    if out is None or lse is None:
+        raise ValueError("rank_forward_accumulate needs the running out and lse tensors")
+    if doc_start is not None:
+        if not causal:
+            raise ValueError("a document mask needs causal=True")
+        _check_doc(doc_start, c, k_blocks)
+    return _forward(q, k_blocks, v_blocks, doc_start, c, rank, causal, zigzag, round_begin, round_end, out, lse,
+                    True, accumulate=True)
+
+
+def _check_doc(doc_start, c, k_blocks):
     import torch
     if not doc_start.is_cuda or doc_start.dtype != torch.int32 or not doc_start.is_contiguous():
         raise ValueError("doc_start must be a contiguous int32 GPU tensor")
     if doc_start.dim() != 1 or doc_start.numel() != c * k_blocks.shape[3]:
         raise ValueError(f"doc_start needs c * n = {c * k_blocks.shape[3]} entries, got {tuple(doc_start.shape)}")
-    return _forward(q, k_blocks, v_blocks, doc_start, c, rank, True, zigzag, round_begin, round_end, out, lse,
-                    with_lse)
 
 
-def _forward(q, k_blocks, v_blocks, doc_start, c, rank, causal, zigzag, round_begin, round_end, out, lse, with_lse):
+def _forward(q, k_blocks, v_blocks, doc_start, c, rank, causal, zigzag, round_begin, round_end, out, lse, with_lse,
+             accumulate=False):
     import torch
     if round_end is None:
         round_end = c
@@ -93,7 +120,12 @@ def _forward(q, k_blocks, v_blocks, doc_start, c, rank, causal, zigzag, round_be
         lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
     elif lse is not None and (lse.shape != (B, hq, nq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, Nq]")
-    if doc_start is None:
+    if accumulate:
+        code = _binding.ra_rank_forward_accumulate(_ptr(q), _ptr(k_blocks), _ptr(v_blocks), _ptr(doc_start),
+                                                   _ptr(out), _ptr(lse), B, hq, hkv, nq, nkv, d, c, rank, causal,
+                                                   zigzag, round_begin, round_end, dt, _stream_handle(q.device))
+        _binding.check(code, "ra_rank_forward_accumulate")
+    elif doc_start is None:
         code = _binding.ra_rank_forward(_ptr(q), _ptr(k_blocks), _ptr(v_blocks), _ptr(out), _ptr(lse),
                                         B, hq, hkv, nq, nkv, d, c, rank, causal, zigzag, round_begin, round_end, dt,
                                         _stream_handle(q.device))

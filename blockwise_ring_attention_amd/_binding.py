@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(_HERE, "libra.so")
 RA_BF16, RA_F32 = 0, 1
 RA_OK, RA_ERR_ARG, RA_ERR_SHAPE, RA_ERR_UNSUPPORTED, RA_ERR_ALIGN, RA_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 # Names every build of the library exports (the entry points include/ra.h declares).
-EXPORTED = ("ra_rank_forward", "ra_rank_forward_doc", "ra_merge", "ra_last_error", "ra_version")
+EXPORTED = ("ra_rank_forward", "ra_rank_forward_doc", "ra_rank_forward_accumulate", "ra_merge", "ra_last_error",
+            "ra_version")
 
 _lib = None
 
@@ -46,6 +47,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.ra_rank_forward.restype = ci
     lib.ra_rank_forward_doc.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 12 + [vp]
     lib.ra_rank_forward_doc.restype = ci
+    lib.ra_rank_forward_accumulate.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 13 + [vp]
+    lib.ra_rank_forward_accumulate.restype = ci
     lib.ra_merge.argtypes = [vp, vp, vp, vp, vp, vp, cll, ci, ci, vp]
     lib.ra_merge.restype = ci
     lib.ra_last_error.argtypes = []
@@ -86,6 +89,14 @@ def ra_rank_forward_doc(q, k_blocks, v_blocks, doc_start, out, lse, batch, hq, h
     """Raw call with integer pointers; returns the status code."""
     return load().ra_rank_forward_doc(q, k_blocks, v_blocks, doc_start, out, lse, batch, hq, hkv, nq, nkv, head_dim,
                                       c, rank, int(zigzag), round_begin, round_end, dtype, stream)
+
+
+def ra_rank_forward_accumulate(q, k_blocks, v_blocks, doc_start, out, lse, batch, hq, hkv, nq, nkv, head_dim, c,
+                               rank, causal, zigzag, round_begin, round_end, dtype, stream) -> int:
+    """Raw call with integer pointers (doc_start 0 or None: no document mask)."""
+    return load().ra_rank_forward_accumulate(q, k_blocks, v_blocks, doc_start or None, out, lse, batch, hq, hkv, nq,
+                                             nkv, head_dim, c, rank, int(causal), int(zigzag), round_begin,
+                                             round_end, dtype, stream)
 
 
 def ra_merge(out_a, lse_a, out_b, lse_b, out, lse, rows, head_dim, dtype, stream) -> int:

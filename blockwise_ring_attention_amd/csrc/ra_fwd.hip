@@ -38,6 +38,7 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kTau = 8.0f;
 constexpr float kBig = 256.0f;   // 2^kTau
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
 // Initial exponent reference of the bf16 fold: finite, far below any finite scaled score,
 // so the first unmasked exponential overflows and raises the reference (see pipe_step).
 constexpr float kRef0 = -1.0e30f;
@@ -218,6 +219,30 @@ __device__ inline float xhalf_sum(float x) {
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Epilogue of one launch for one row: the launch's partial is O / lt with lse_new
+// (natural log) from the row sum lt taken against the reference mref (log2 units).
+// Without accumulation the row gets exactly that. With accumulation the partial is folded
+// into the running (out, lse) already in memory, a result over a disjoint key set: with
+// M = max(lse_old, lse_new) and weights e^(lse - M), out = (w_old out_old + w_new out_new)
+// / (w_old + w_new) and lse = M + ln(w_old + w_new) ("What do you do about long sequences
+// and sparse models?", section "How does attention survive being split?"). Returned as
+// factors: merged out = c_old * out_old + c_new * O.
+struct RowFold {
+  float c_old, c_new, lse;
+};
+
+__device__ inline RowFold fold_row(bool accumulate, float lse_old, float mref, float lt) {
+  const float lse_new = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (!accumulate) return RowFold{0.f, inv, lse_new};
+  const float m = fmaxf(lse_old, lse_new);
+  if (m == kNegInf) return RowFold{0.f, 0.f, kNegInf};
+  const float w_old = fast_exp2((lse_old - m) * kLog2e);
+  const float w_new = fast_exp2((lse_new - m) * kLog2e);
+  const float tot = w_old + w_new;
+  return RowFold{w_old / tot, w_new / tot * inv, m + __builtin_amdgcn_logf(tot) * kLn2};
+}
 
 // ---------------------------------------------------------------- bf16 kernel
 // A workgroup is 8 waves, one 32-query column block each, and fills a CU (two waves per
@@ -668,22 +693,30 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
-  // Epilogue: out = O / sum, lse = ln(sum) + reference.
+  // Epilogue: out = O / sum, lse = ln(sum) + reference, or (accumulate) those folded into
+  // the running result in memory.
   const float lt = xhalf_sum(lsum);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (!rvalid) return;
   const size_t ridx = ((size_t)tile.b * a.hq + head) * a.nq + row;
   __bf16* orow = static_cast<__bf16*>(a.out) + ridx * D;
+  const RowFold f = fold_row(a.acc != 0, a.acc ? a.lse[ridx] : 0.f, mref, lt);
 #pragma unroll
   for (int dv = 0; dv < NDV; ++dv)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      bf16x4* dst = reinterpret_cast<bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf);
       bf16x4 w;
+      if (f.c_old != 0.f) {  // rows with nothing folded yet (lse -inf) never read out
+        const bf16x4 old = *dst;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(o[dv][4 * i + jj] * inv);
-      *reinterpret_cast<bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf) = w;
+        for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(f.c_old * (float)old[jj] + f.c_new * o[dv][4 * i + jj]);
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(o[dv][4 * i + jj] * f.c_new);
+      }
+      *dst = w;
     }
-  if (a.lse != nullptr && hf == 0) a.lse[ridx] = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+  if (a.lse != nullptr && hf == 0) a.lse[ridx] = f.lse;
 }
 
 // ---------------------------------------------------------------- fp32 kernel
@@ -786,22 +819,25 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   }
 
   const float lt = xhalf_sum(lsum);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (!rvalid) return;
   const size_t ridx = ((size_t)tile.b * a.hq + head) * a.nq + row;
   float* orow = og + ridx * d;
+  const RowFold f = fold_row(a.acc != 0, a.acc ? a.lse[ridx] : 0.f, mref, lt);
 #pragma unroll
   for (int dv = 0; dv < DP / 32; ++dv)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c0 = 32 * dv + 8 * i + 4 * hf;
       if (c0 < d) {
-        const f32x4 w = {o[dv][4 * i] * inv, o[dv][4 * i + 1] * inv, o[dv][4 * i + 2] * inv, o[dv][4 * i + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + c0) = w;
+        f32x4* dst = reinterpret_cast<f32x4*>(orow + c0);
+        const f32x4 old = f.c_old != 0.f ? *dst : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 w;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) w[jj] = f.c_old * old[jj] + f.c_new * o[dv][4 * i + jj];
+        *dst = w;
       }
     }
-  if (a.lse != nullptr && hf == 0)
-    a.lse[ridx] = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+  if (a.lse != nullptr && hf == 0) a.lse[ridx] = f.lse;
 }
 
 }  // namespace

@@ -49,11 +49,11 @@ extern "C" int ra_version(void) { return 200; }  // 0.2.0
 
 namespace {
 
-// Both forward entry points: checks, work planning and the launch. `doc` is null for
-// ra_rank_forward; for ra_rank_forward_doc it holds the document starts (causal).
+// Every forward entry point: checks, work planning and the launch. `doc` is null unless a
+// document mask applies (then causal); `acc` folds the result into the running (out, lse).
 int forward(const void* q, const void* k_blocks, const void* v_blocks, const int* doc, void* out, float* lse,
             int batch, int hq, int hkv, int nq, int nkv, int head_dim, int c, int rank, int causal, int zigzag,
-            int round_begin, int round_end, int dtype, void* stream) {
+            int round_begin, int round_end, int dtype, void* stream, bool acc = false) {
   if (dtype != RA_BF16 && dtype != RA_F32) return fail(RA_ERR_ARG, "unknown dtype %d", dtype);
   if (batch < 0 || nq < 0 || nkv < 0) return fail(RA_ERR_ARG, "negative size (batch=%d nq=%d nkv=%d)", batch, nq, nkv);
   if (hq < 1 || hkv < 1) return fail(RA_ERR_ARG, "hq=%d and hkv=%d must be >= 1", hq, hkv);
@@ -83,9 +83,10 @@ int forward(const void* q, const void* k_blocks, const void* v_blocks, const int
     return fail(RA_ERR_ALIGN, "q, k_blocks, v_blocks and out must be 16-byte aligned");
   if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
   if (!aligned(doc, 4)) return fail(RA_ERR_ALIGN, "doc_start must be 4-byte aligned");
+  if (acc && lse == nullptr) return fail(RA_ERR_ARG, "accumulating needs the running lse (got NULL)");
 
   ra::FwdArgs a{};
-  a.q = q; a.k = k_blocks; a.v = v_blocks; a.out = out; a.lse = lse; a.doc = doc;
+  a.q = q; a.k = k_blocks; a.v = v_blocks; a.out = out; a.lse = lse; a.doc = doc; a.acc = acc ? 1 : 0;
   a.B = batch; a.hq = hq; a.hkv = hkv; a.nq = nq; a.nkv = nkv; a.d = head_dim;
   a.c = c; a.rank = rank; a.causal = is_causal; a.zigzag = is_zigzag; a.t0 = round_begin; a.t1 = round_end;
   const int col_blocks = dtype == RA_BF16 ? ra::kBf16ColBlocks : ra::kF32ColBlocks;
@@ -126,6 +127,15 @@ extern "C" int ra_rank_forward_doc(const void* q, const void* k_blocks, const vo
   if (doc_start == nullptr && batch > 0 && nq > 0) return fail(RA_ERR_ARG, "doc_start must not be NULL");
   return forward(q, k_blocks, v_blocks, doc_start, out, lse, batch, hq, hkv, nq, nkv, head_dim, c, rank, 1, zigzag,
                  round_begin, round_end, dtype, stream);
+}
+
+extern "C" int ra_rank_forward_accumulate(const void* q, const void* k_blocks, const void* v_blocks,
+                                          const int* doc_start, void* out, float* lse, int batch, int hq, int hkv,
+                                          int nq, int nkv, int head_dim, int c, int rank, int causal, int zigzag,
+                                          int round_begin, int round_end, int dtype, void* stream) {
+  if (doc_start != nullptr && causal == 0) return fail(RA_ERR_ARG, "a document mask needs causal=1");
+  return forward(q, k_blocks, v_blocks, doc_start, out, lse, batch, hq, hkv, nq, nkv, head_dim, c, rank, causal,
+                 zigzag, round_begin, round_end, dtype, stream, true);
 }
 
 extern "C" int ra_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,

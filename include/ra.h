@@ -122,6 +122,38 @@ int ra_rank_forward_doc(const void* q, const void* k_blocks, const void* v_block
                         int dtype, void* stream);
 
 /*
+ * ra_rank_forward_accumulate -- ra_rank_forward (or, with doc_start, ra_rank_forward_doc)
+ * over rounds [round_begin, round_end) whose result is folded into the running result
+ * already held in (out, lse) instead of overwriting it. This is one step of the streamed
+ * ring: each round's partial joins the accumulator as its block arrives, combined
+ * exactly through the maxima and sums of both ("What do you do about long sequences and
+ * sparse models?", section "How does attention survive being split?"), with no separate
+ * merge launch or partial buffer.
+ *
+ *   out [batch, hq, nq, head_dim], dtype, device: in, the running output; out, the
+ *       output over the union of its keys and this call's. Where the incoming lse is
+ *       -inf the incoming out is never read (it may hold anything).
+ *   lse [batch, hq, nq] fp32, device: in, the running lse (set it to -inf before the
+ *       first call); out, the lse over the union. Must not be NULL.
+ *   doc_start: NULL for no document mask, else as in ra_rank_forward_doc (then causal
+ *       must be 1).
+ *
+ * The folded result equals ra_merge of the accumulator with this call's ra_rank_forward
+ * result: for M = max(lse_old, lse_new), M = -inf gives out = 0 and lse = -inf; else
+ * w = e^(lse - M) for each side, out = (w_old out_old + w_new out_new) / (w_old + w_new),
+ * lse = M + ln(w_old + w_new). The call's rounds must hold keys disjoint from those
+ * already folded in (a ring visits each block once). Every other argument, layout and
+ * error is that of ra_rank_forward, plus RA_ERR_ARG for a NULL lse or for doc_start with
+ * causal = 0. An empty round range leaves (out, lse) unchanged.
+ */
+int ra_rank_forward_accumulate(const void* q, const void* k_blocks, const void* v_blocks,
+                               const int* doc_start, void* out, float* lse,
+                               int batch, int hq, int hkv, int nq, int nkv, int head_dim,
+                               int c, int rank, int causal, int zigzag,
+                               int round_begin, int round_end,
+                               int dtype, void* stream);
+
+/*
  * ra_merge -- combine two partial results over disjoint key sets into the result over
  * their union ("What do you do about long sequences and sparse models?", section "How
  * does attention survive being split?": partials combine exactly through their

@@ -103,6 +103,36 @@ def test_forward_doc_empty_is_a_noop(ra_lib):
     assert _fwd_doc(nq=0, nkv=0, q=0, k=0, v=0, doc=0, out=0, lse=0) == B.RA_OK
 
 
+def _fwd_acc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, doc=0, out=FAKE, lse=FAKE, batch=1, hq=4, hkv=2, nq=64, nkv=64, d=128, c=4,
+             rank=1, causal=1, zigzag=1, t0=0, t1=4, dtype=B.RA_BF16)
+    a.update(kw)
+    return B.ra_rank_forward_accumulate(a["q"], a["k"], a["v"], a["doc"], a["out"], a["lse"], a["batch"], a["hq"],
+                                        a["hkv"], a["nq"], a["nkv"], a["d"], a["c"], a["rank"], a["causal"],
+                                        a["zigzag"], a["t0"], a["t1"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=0), B.RA_ERR_ARG),                    # the running lse is required
+    (dict(lse=0, doc=FAKE), B.RA_ERR_ARG),
+    (dict(doc=FAKE, causal=0), B.RA_ERR_ARG),       # the document mask is causal
+    (dict(doc=FAKE + 2), B.RA_ERR_ALIGN),
+    (dict(lse=FAKE + 2), B.RA_ERR_ALIGN),
+    (dict(t0=2, t1=1), B.RA_ERR_ARG),
+    (dict(nkv=32), B.RA_ERR_SHAPE),
+    (dict(d=96), B.RA_ERR_UNSUPPORTED),
+    (dict(out=0), B.RA_ERR_ARG),
+])
+def test_forward_accumulate_argument_errors(ra_lib, kw, code):
+    assert _fwd_acc(**kw) == code
+    assert B.last_error() != ""
+
+
+def test_forward_accumulate_empty_is_a_noop(ra_lib):
+    assert _fwd_acc(batch=0, q=0, k=0, v=0, out=0, lse=0) == B.RA_OK
+    assert _fwd_acc(nq=0, nkv=0, q=0, k=0, v=0, out=0, lse=0, causal=0) == B.RA_OK
+
+
 def test_forward_empty_is_a_noop(ra_lib):
     assert _fwd(nq=0, nkv=0, q=0, k=0, v=0, out=0, lse=0, causal=0) == B.RA_OK
     assert _fwd(batch=0, q=0, k=0, v=0, out=0, lse=0) == B.RA_OK

@@ -1,0 +1,122 @@
+"""GPU parity of the streamed ring (ra_rank_forward_accumulate, through the C ABI): a rank
+folds each arriving block into its running (out, lse) as the ring turns, and after the
+last round holds the result over the whole ring ("What do you do about long sequences and
+sparse models?", section "How does attention survive being split?").
+
+Checked against the fp64 oracle's full-ring result: one launch per round in ring order,
+rounds in uneven groups, rounds in reverse order (the fold is exact in any order), with
+and without the document mask, both dtypes. The accumulator starts as lse = -inf with
+out holding NaN, which must never be read. An empty round range leaves (out, lse)
+bit-identical, and one fold equals ra_merge of the accumulator with the same rounds'
+ra_rank_forward result."""
+
+import numpy as np
+import pytest
+
+import oracle
+from blockwise_ring_attention_amd.inputs import doc_start_from_lengths, draw_document_lengths, random_array
+from tests.gpu_util import assert_parity, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, hq, hkv, d, n, c, rank, causal, zigzag, dtype, doc
+    (1, 8, 1, 128, 512, 4, 1, True, True, "bf16", False),
+    (1, 8, 2, 128, 256, 4, 0, True, False, "bf16", False),   # rank 0: rounds 1.. see no keys
+    (1, 8, 2, 128, 256, 4, 3, True, False, "bf16", False),
+    (2, 4, 2, 64, 136, 3, 2, False, False, "bf16", False),   # non-causal, ragged tiles
+    (1, 16, 1, 128, 96, 2, 1, True, True, "bf16", False),    # two head sets
+    (1, 8, 2, 128, 512, 4, 2, True, True, "bf16", True),
+    (1, 4, 1, 128, 200, 3, 0, True, True, "bf16", True),     # ragged chunks (m = 100)
+    (1, 2, 1, 64, 128, 4, 3, True, True, "f32", False),
+    (2, 3, 1, 24, 72, 3, 0, True, False, "f32", False),
+    (1, 2, 2, 96, 128, 4, 1, True, True, "f32", True),
+]
+
+GROUPINGS = {
+    "per_round": lambda c: [(t, t + 1) for t in range(c)],
+    "grouped": lambda c: [(0, 1), (1, c - 1), (c - 1, c)] if c > 2 else [(0, 1), (1, c)],
+    "reverse": lambda c: [(t, t + 1) for t in reversed(range(c))],
+}
+
+
+def _inputs(B, hq, hkv, d, n, c, dtype, doc, seed):
+    q = random_array((B, hq, n, d), dtype, seed)
+    k = random_array((c, B, hkv, n, d), dtype, seed + 1)
+    v = random_array((c, B, hkv, n, d), dtype, seed + 2)
+    ds = doc_start_from_lengths(draw_document_lengths(c * n, 37, 1.2, seed)) if doc else None
+    return q, k, v, ds
+
+
+def _device(q, k, v, ds, dtype):
+    import torch
+    dd = torch.from_numpy(np.ascontiguousarray(ds, dtype=np.int32)).cuda() if ds is not None else None
+    return to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), dd
+
+
+def _fresh_accumulator(qd):
+    import torch
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full(qd.shape[:3], float("-inf"), dtype=torch.float32, device=qd.device)
+    return out, lse
+
+
+def _host(out, lse):
+    import torch
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("grouping", sorted(GROUPINGS))
+@pytest.mark.parametrize("B,hq,hkv,d,n,c,rank,causal,zigzag,dtype,doc", CASES)
+def test_streamed_ring_parity(B, hq, hkv, d, n, c, rank, causal, zigzag, dtype, doc, grouping):
+    import blockwise_ring_attention_amd as ra
+    say(f"accumulate {grouping} B={B} hq={hq} hkv={hkv} d={d} n={n} c={c} rank={rank} causal={causal} "
+        f"zigzag={zigzag} {dtype} doc={doc}")
+    q, k, v, ds = _inputs(B, hq, hkv, d, n, c, dtype, doc, 1300 + n + c + rank)
+    qd, kd, vd, dd = _device(q, k, v, ds, dtype)
+    out, lse = _fresh_accumulator(qd)
+    for t0, t1 in GROUPINGS[grouping](c):
+        ra.rank_forward_accumulate(qd, kd, vd, out, lse, c, rank, causal, zigzag, t0, t1, doc_start=dd)
+    o, l = _host(out, lse)
+    ref, ref_lse = oracle.rank_forward(q, k, v, c, rank, causal, zigzag, doc_start=ds)
+    assert_parity(o, ref, l, ref_lse, dtype, f"accumulate {grouping}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_round_range_leaves_accumulator(dtype):
+    import torch
+    import blockwise_ring_attention_amd as ra
+    c, n, rank = 4, 256, 1
+    q, k, v, _ = _inputs(1, 4, 2, 128 if dtype == "bf16" else 64, n, c, dtype, False, 41)
+    qd, kd, vd, _ = _device(q, k, v, None, dtype)
+    out, lse = _fresh_accumulator(qd)
+    ra.rank_forward_accumulate(qd, kd, vd, out, lse, c, rank, True, True, 0, 2)
+    before_out, before_lse = out.clone(), lse.clone()
+    ra.rank_forward_accumulate(qd, kd, vd, out, lse, c, rank, True, True, 2, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, before_out) and torch.equal(lse, before_lse)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fold_equals_merge_of_partials(dtype):
+    """One accumulate call over rounds [2, c) == ra_merge(accumulator, ra_rank_forward over
+    [2, c)): the kernel's epilogue and the merge kernel take the same combination."""
+    import torch
+    import blockwise_ring_attention_amd as ra
+    c, n, rank, d = 4, 384, 2, 128 if dtype == "bf16" else 64
+    q, k, v, _ = _inputs(1, 8, 2, d, n, c, dtype, False, 57)
+    qd, kd, vd, _ = _device(q, k, v, None, dtype)
+    out, lse = _fresh_accumulator(qd)
+    ra.rank_forward_accumulate(qd, kd, vd, out, lse, c, rank, True, True, 0, 2)
+    acc_out, acc_lse = out.clone(), lse.clone()
+    ra.rank_forward_accumulate(qd, kd, vd, out, lse, c, rank, True, True, 2, c)
+    part_out, part_lse = ra.rank_forward(qd, kd, vd, c, rank, True, True, 2, c)
+    m_out, m_lse = ra.merge(acc_out, acc_lse, part_out, part_lse)
+    torch.cuda.synchronize()
+    diff = (out.float() - m_out.float()).abs().max().item()
+    # bf16: the merge rounds the partial to bf16 before combining, the fold does not, so
+    # the two may differ by about one bf16 step (2^-7 relative) of the output values.
+    scale = max(1.0, m_out.float().abs().max().item())
+    assert diff <= (2.0 ** -6 * scale if dtype == "bf16" else 1e-6), diff
+    assert torch.allclose(lse, m_lse, rtol=0, atol=1e-5)
