@@ -29,11 +29,16 @@ PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 matrix
 METRIC = "attention TFLOP/s (unmasked) per rank share, 1 GPU; % of bf16 MFMA peak"
 DEFAULT_WORKLOAD = "gqa64x8_d128_s128k_c16_zigzag_bf16"
 ALSO_WORKLOADS = ["gqa32x8_d128_s32k_c8_zigzag_bf16"]
-KERNEL_SOURCE = os.path.join(ROOT, "blockwise_ring_attention_amd", "csrc", "ra_fwd.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_ring_attention_amd", "csrc", f)
+                  for f in ("ra_fwd.hip", "ra_internal.h")]
 
 
 def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    """sha256[:16] over the forward kernel's sources (the kernel file, then its header)."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, launch_ms: float):
