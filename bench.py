@@ -21,6 +21,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -28,7 +30,8 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x
 PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 matrix
 METRIC = "attention TFLOP/s (unmasked) per rank share, 1 GPU; % of bf16 MFMA peak"
 DEFAULT_WORKLOAD = "gqa64x8_d128_s128k_c16_zigzag_bf16"
-ALSO_WORKLOADS = ["gqa32x8_d128_s32k_c8_zigzag_bf16"]
+ALSO_WORKLOADS = ["gqa32x8_d128_s32k_c8_zigzag_bf16", "mha16_b2_d128_s64k_c8_noncausal_outliers_bf16"]
+MIN_TIMED_MS = 200.0   # short workloads get more steps so the timed region spans this much
 KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_ring_attention_amd", "csrc", f)
                   for f in ("ra_fwd.hip", "ra_internal.h")]
 
@@ -100,7 +103,7 @@ def time_workload(w, steps: int, warmup: int, arrays=None):
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     del qd, kd, vd, out, lse
     torch.cuda.empty_cache()
-    return wall / steps * 1e3, sum(launch_ms) / len(launch_ms), min(launch_ms)
+    return wall / steps * 1e3, sum(launch_ms) / len(launch_ms), min(launch_ms), float(np.median(launch_ms))
 
 
 def _device_inputs(w, arrays):
@@ -224,7 +227,7 @@ def balance_sweep(w, steps: int, warmup: int):
         ranks = []
         for r in range(w.c):
             wr = dataclasses.replace(w, rank=r, zigzag=zig)
-            ms, ml, mn = time_workload(wr, steps, warmup, arrays)
+            ms, ml, mn, _ = time_workload(wr, steps, warmup, arrays)
             if ds is None:
                 e = acc.allowed_entries(w.c, r, w.rows, w.rows, True, zig)
             else:
@@ -348,7 +351,7 @@ def main():
         return
     flop, nbytes = workload_numbers(w)
     arrays = make_inputs(w)
-    ms_step, ms_launch, ms_min = time_workload(w, args.steps, args.warmup, arrays)
+    ms_step, ms_launch, ms_min, ms_med = time_workload(w, args.steps, args.warmup, arrays)
     value = flop / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flop / (ms_launch * 1e-3) / 1e12
@@ -374,15 +377,22 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "algorithmic_bytes": nbytes, "kernel_ms_avg": round(ms_launch, 4),
-                     "kernel_ms_min": round(ms_min, 4)},
+                     "kernel_ms_min": round(ms_min, 4), "kernel_ms_median": round(ms_med, 4)},
     }
     if not args.no_also:
         also = []
         for name in ALSO_WORKLOADS:
             wa = WORKLOADS[name]
             fa, _ = workload_numbers(wa)
-            ms_a, ml_a, _ = time_workload(wa, args.steps, args.warmup)
+            arrays_a = make_inputs(wa)
+            ms_a, ml_a, _, _ = time_workload(wa, args.steps, args.warmup, arrays_a)
+            steps_a = args.steps
+            if steps_a * ms_a < MIN_TIMED_MS:   # too short to time well: run again with more steps
+                steps_a = int(np.ceil(MIN_TIMED_MS / ms_a))
+                ms_a, ml_a, _, _ = time_workload(wa, steps_a, args.warmup, arrays_a)
+            del arrays_a
             also.append({"workload": name, "value": round(fa / (ms_a * 1e-3) / 1e12, 2), "ms_per_step": round(ms_a, 4),
+                         "kernel_ms_avg": round(ml_a, 4), "steps": steps_a,
                          "pct_of_peak": round(100 * fa / (ms_a * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)})
         line["also"] = also
     if not args.no_per_round:

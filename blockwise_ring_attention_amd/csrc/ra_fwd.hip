@@ -410,39 +410,76 @@ __device__ inline void mask_sub(const FwdArgs& a, const SubInfo& si, int hf, int
 //       16-31) (2*NDV MFMAs, one per value block and key half);
 //   SM: e = 2^(sc * S - ref) for sub-tile t (sc_ = S^T of t) and its lane sum ps.
 // Step i pairs QK k-step i with P.V product i and two (D = 128) or four (D = 64) of the
-// sixteen exponentials; LDS fragment reads run two steps ahead of their MFMAs. The
-// scheduling groups pin that interleave.
-template <int D, bool QK, bool PV, bool SM>
-__device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const bf16x8 (&qf)[D / 16],
-                                           const int (&koff)[D / 16], const int (&voff)[D / 32],
-                                           const bf16x8 (&pp)[2], f32x16 (&o)[D / 32], f32x16& sn,
-                                           const f32x16& sc_, float sc, float nm, f32x16& e, float& ps) {
+// sixteen exponentials; LDS fragment reads run kAhead products ahead of their MFMAs, also
+// across steps: the last products of a step read the first fragments of the next one
+// (NXK: its K fragments from kn, NXV: its V^T fragments from vn), and a step whose first
+// fragments were read that way (PRK, PRV) starts on them at once. The scheduling groups
+// pin the interleave. A stage's first step has only its V^T fragments read ahead (its K
+// tile is complete only after the stage barrier); it issues each P.V product before its
+// QK k-step, so the matrix cores start while the first K fragments are in flight.
+constexpr int kAhead = 2;
+
+template <int D>
+struct Frags {
+  bf16x8 kf[D / 16];
+  s16x4 vlo[D / 16], vhi[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void read_k(const char* kt, const int (&koff)[D / 16], int i, int slot, Frags<D>& f) {
+  f.kf[slot] = *reinterpret_cast<const bf16x8*>(kt + koff[i]);
+}
+
+template <int D>
+__device__ __forceinline__ void read_vt(const char* vt, const int (&voff)[D / 32], int i, int slot, Frags<D>& f) {
+  using L = Bf16Layout<D>;
+  const int dv = i % L::NDV, ss = i / L::NDV;
+  const char* vb = vt - L::kVBias + ss * 16 * L::ROWB;   // voff carries +kVBias
+  f.vlo[slot] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[dv]));
+  f.vhi[slot] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * L::ROWB + voff[dv]));
+}
+
+template <int D, bool QK, bool PV, bool SM, bool PRK, bool PRV, bool NXK, bool NXV>
+__device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const char* kn, const char* vn,
+                                           const bf16x8 (&qf)[D / 16], const int (&koff)[D / 16],
+                                           const int (&voff)[D / 32], const bf16x8 (&pp)[2], f32x16 (&o)[D / 32],
+                                           f32x16& sn, const f32x16& sc_, float sc, float nm, f32x16& e, float& ps,
+                                           Frags<D>& f) {
   using L = Bf16Layout<D>;
   constexpr int NKS = L::NKS, NDV = L::NDV;
   static_assert(NKS == 2 * NDV, "one P.V product per QK k-step");
+  static_assert((!PRK || QK) && (!PRV || PV), "fragments read ahead for a product the step does not make");
   constexpr int EPS = 16 / NKS;                       // exponentials per step
   constexpr int READS = (QK ? 1 : 0) + (PV ? 2 : 0);  // LDS reads per step
-  constexpr int AHEAD = 2;
-  bf16x8 kf[NKS];
-  s16x4 vlo[NKS], vhi[NKS];
-  auto load = [&](int i) {
-    if (QK) kf[i] = *reinterpret_cast<const bf16x8*>(kt + koff[i]);
-    if (PV) {
-      const int dv = i % NDV, ss = i / NDV;
-      const char* vb = vt - L::kVBias + ss * 16 * L::ROWB;   // voff carries +kVBias
-      vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[dv]));
-      vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * L::ROWB + voff[dv]));
-    }
-  };
+  constexpr int NEXT = (NXK ? 1 : 0) + (NXV ? 2 : 0);
+  constexpr int AHEAD = kAhead;
+  constexpr bool PVFIRST = PRV && !PRK;
 #pragma unroll
-  for (int i = 0; i < AHEAD; ++i) load(i);
-  if (READS) __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * READS, 0);
+  for (int i = 0; i < AHEAD; ++i) {
+    if (QK && !PRK) read_k<D>(kt, koff, i, i, f);
+    if (PV && !PRV) read_vt<D>(vt, voff, i, i, f);
+  }
+  constexpr int FIRST = AHEAD * ((QK && !PRK ? 1 : 0) + (PV && !PRV ? 2 : 0));
+  if (FIRST) __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
   if (QK) sn = f32x16{};
   ps = 0.f;
 #pragma unroll
   for (int i = 0; i < NKS; ++i) {
-    if (i + AHEAD < NKS) load(i + AHEAD);
-    if (QK) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], sn, 0, 0, 0);
+    const int j = i + AHEAD;   // the fragment read in this product's slot of the schedule
+    if (j < NKS) {
+      if (QK) read_k<D>(kt, koff, j, j, f);
+      if (PV) read_vt<D>(vt, voff, j, j, f);
+    } else {
+      if (NXK) read_k<D>(kn, koff, j - NKS, j - NKS, f);
+      if (NXV) read_vt<D>(vn, voff, j - NKS, j - NKS, f);
+    }
+    auto pv = [&]() {
+      const int dv = i % NDV, ss = i / NDV;
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f.vlo[i], f.vhi[i], 0, 1, 2, 3, 4, 5, 6, 7));
+      o[dv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[ss], o[dv], 0, 0, 0);
+    };
+    if (PV && PVFIRST) pv();
+    if (QK) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kf[i], qf[i], sn, 0, 0, 0);
     if (SM) {
 #pragma unroll
       for (int k = 0; k < EPS; ++k) {
@@ -451,16 +488,22 @@ __device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const
         ps += e[x];
       }
     }
-    if (PV) {
-      const int dv = i % NDV, ss = i / NDV;
-      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7));
-      o[dv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[ss], o[dv], 0, 0, 0);
+    if (PV && !PVFIRST) pv();
+    if (PVFIRST) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // P.V product i
+      if (SM) __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS / 2, 0);
+      if (QK) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // QK k-step i
+    } else {
+      if (QK) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (SM) __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS / 2, 0);
+      if (PV) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    if (QK) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (SM) __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS / 2, 0);
-    if (PV) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (SM) __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS - 3 * EPS / 2, 0);
-    if (READS && i + AHEAD < NKS) __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+    if (j < NKS) {
+      if (READS) __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+    } else {
+      if (NEXT) __builtin_amdgcn_sched_group_barrier(0x100, NEXT, 0);
+    }
   }
 }
 
@@ -473,18 +516,20 @@ __device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const
 // whose exponential overflows -- the wave takes the row maximum, raises the reference,
 // rescales O (which already holds the P.V products issued in this step, taken against
 // the old reference) and the sum, and recomputes p. Masked scores are -inf and give 0.
-template <int D, bool QK, bool PV, bool SM>
+template <int D, bool QK, bool PV, bool SM, bool PRK = false, bool PRV = false, bool NXK = false,
+          bool NXV = false>
 __device__ __forceinline__ void pipe_step(const FwdArgs& a, const SubInfo& si, int hf, int qds, int qpos, float sc,
                                           const char* kt, const char* vt, const bf16x8 (&qf)[D / 16],
                                           const int (&koff)[D / 16], const int (&voff)[D / 32],
                                           const bf16x8 (&pp)[2], f32x16 (&o)[D / 32], f32x16& sn, f32x16& scur,
-                                          bf16x8 (&pc)[2], float& mref, float& lsum) {
+                                          bf16x8 (&pc)[2], float& mref, float& lsum, Frags<D>& f,
+                                          const char* kn = nullptr, const char* vn = nullptr) {
   constexpr int NDV = D / 32;
   if (SM && si.mask) mask_sub(a, si, hf, qpos, qds, scur);
   const float nm = -mref;
   f32x16 e;
   float ps;
-  pipe_block<D, QK, PV, SM>(kt, vt, qf, koff, voff, pp, o, sn, scur, sc, nm, e, ps);
+  pipe_block<D, QK, PV, SM, PRK, PRV, NXK, NXV>(kt, vt, kn, vn, qf, koff, voff, pp, o, sn, scur, sc, nm, e, ps, f);
   if (SM) {
     if (__builtin_amdgcn_ballot_w64(ps > kBig)) {
       float mx = scur[0];
@@ -625,6 +670,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   if (cc.valid) {
     f32x16 sA, sB;
     bf16x8 pA[2], pB[2];
+    Frags<D> fr;   // LDS fragments in flight, read ahead across steps (see pipe_block)
     // ---- stage 0 (buffer 0): steps -1 and 0
     wait_stages<D>(issued - 1);
     phase_barrier();
@@ -635,9 +681,11 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     }
     SubInfo prev = sub_info(cc, 1);
     pipe_step<D, true, false, false>(a, prev, hf, qds, qpos, sc, kb[0], vb[0], qf, koff, voff, pB, o, sA, sB, pB,
-                                     mref, lsum);
-    pipe_step<D, true, false, true>(a, sub_info(cc, 0), hf, qds, qpos, sc, kb[0] + 32 * L::ROWB, vb[0], qf, koff,
-                                    voff, pB, o, sB, sA, pA, mref, lsum);
+                                     mref, lsum, fr);
+    // ... and reads the first V^T fragments of stage 0 for step 1
+    pipe_step<D, true, false, true, false, false, false, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
+                                                               kb[0] + 32 * L::ROWB, vb[0], qf, koff, voff, pB, o,
+                                                               sB, sA, pA, mref, lsum, fr, nullptr, vb[0]);
     cc.next(a, qr);
     int s = 1;
     int last = 0;   // buffer of the last stage, for the tail
@@ -647,6 +695,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
         for (int u = 0; u < NB; ++u) {
           // ---- stage s (buffer b); prev describes sub-tile 1 of stage s - 1 (buffer bp)
           const int b = (1 + u) % NB, bp = u % NB;
+          // The first V^T fragments of step 2s-1 (stage s-1's, complete since the last
+          // barrier) were read at the end of step 2s-2; its K fragments wait for this one.
           wait_stages<D>(issued - (s + 1));
           phase_barrier();
           // The K tile of stage s + NB - 2 is issued before step 2s-1 and its V tile before
@@ -659,8 +709,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
             ld.template issue<true, false>(kb[bn], vb[bn], kslab, vslab, load_row, a.nkv);
           }
           // step 2s-1: S of (s, sub 0); P.V of (s-1, sub 0); softmax of (s-1, sub 1)
-          pipe_step<D, true, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf, koff, voff, pA, o, sA, sB, pB,
-                                         mref, lsum);
+          pipe_step<D, true, true, true, false, true, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf, koff,
+                                                                voff, pA, o, sA, sB, pB, mref, lsum, fr,
+                                                                kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB);
           __builtin_amdgcn_sched_barrier(0);
           if (load) {
             ld.template issue<false, true>(kb[bn], vb[bn], kslab, vslab, load_row, a.nkv);
@@ -668,8 +719,11 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
             ++issued;
           }
           // step 2s: S of (s, sub 1); P.V of (s-1, sub 1); softmax of (s, sub 0)
-          pipe_step<D, true, true, true>(a, sub_info(cc, 0), hf, qds, qpos, sc, kb[b] + 32 * L::ROWB,
-                                         vb[bp] + 32 * L::ROWB, qf, koff, voff, pB, o, sB, sA, pA, mref, lsum);
+          // ... and reads the first V^T fragments of stage s for step 2s+1 (or the tail)
+          pipe_step<D, true, true, true, true, true, false, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
+                                                                  kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB, qf,
+                                                                  koff, voff, pB, o, sB, sA, pA, mref, lsum, fr,
+                                                                  nullptr, vb[b]);
           prev = sub_info(cc, 1);
           cc.next(a, qr);
           ++s;
@@ -685,10 +739,12 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (b == last) {
-        pipe_step<D, false, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[b], qf, koff, voff, pA, o, sA, sB, pB,
-                                        mref, lsum);
-        pipe_step<D, false, true, false>(a, prev, hf, qds, qpos, sc, kb[b], vb[b] + 32 * L::ROWB, qf, koff, voff, pB,
-                                         o, sB, sA, pA, mref, lsum);
+        // the first V^T fragments of each step were read by the step before
+        pipe_step<D, false, true, true, false, true, false, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[b], qf, koff,
+                                                                  voff, pA, o, sA, sB, pB, mref, lsum, fr, nullptr,
+                                                                  vb[b] + 32 * L::ROWB);
+        pipe_step<D, false, true, false, false, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[b] + 32 * L::ROWB, qf,
+                                                      koff, voff, pB, o, sB, sA, pA, mref, lsum, fr);
       }
     }
   }
