@@ -358,9 +358,11 @@ __device__ __forceinline__ void wait_stages(int stages) {
 
 // Workgroup barrier between phases. No instruction is scheduled across it, and the
 // memory clobber keeps the compiler from moving loads or stores over it. It waits for no
-// memory counter: every LDS read of a phase feeds an MFMA of the same phase, so it has
-// returned before the wave arrives, and K/V loads are waited for explicitly
-// (wait_stages), which a workgroup fence would instead drain completely.
+// memory counter. The LDS reads still in flight when a wave arrives are the first V^T
+// fragments of the next step, from the stage just folded, whose buffer no load issued
+// after this barrier writes (the next load into it comes two barriers later). K/V loads
+// are waited for explicitly (wait_stages), which a workgroup fence would instead drain
+// completely.
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
