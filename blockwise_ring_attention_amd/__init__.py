@@ -70,7 +70,7 @@ def rank_forward_accumulate(q, k_blocks, v_blocks, out, lse, c: int, rank: int, 
 
     ``out`` [B, Hq, Nq, d] (q's dtype) and ``lse`` [B, Hq, Nq] fp32 hold the result over
     the keys folded so far (lse = -inf where none: start from ``lse.fill_(-inf)``; out
-    is then never read). Afterwards they hold the result over those keys and this call's
+    is then ignored). Afterwards they hold the result over those keys and this call's
     rounds, which must not repeat a round already folded in. ``doc_start`` (optional)
     adds the document mask of ``rank_forward_doc`` (causal only). Returns (out, lse).
     """

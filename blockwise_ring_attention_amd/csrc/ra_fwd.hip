@@ -669,6 +669,25 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
+  // Accumulate mode: the running (out, lse) of the lane's row, read at the start of the
+  // tail (Q fragments are dead by then, so the registers are free) and used by the
+  // epilogue, so the read overlaps the last P.V products instead of following them.
+  const size_t ridx = ((size_t)tile.b * a.hq + head) * a.nq + row;
+  __bf16* const orow = static_cast<__bf16*>(a.out) + ridx * D;
+  bf16x4 oldo[NDV][4] = {};
+  float lse_old = kNegInf;
+  bool have_old = false;
+  auto read_old = [&]() {
+    if (a.acc && rvalid) {
+      lse_old = a.lse[ridx];
+#pragma unroll
+      for (int dv = 0; dv < NDV; ++dv)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oldo[dv][i] = *reinterpret_cast<const bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf);
+    }
+    have_old = true;
+  };
+
   if (cc.valid) {
     f32x16 sA, sB;
     bf16x8 pA[2], pB[2];
@@ -737,6 +756,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
       }
     }
   tail:
+    read_old();
     // ---- after the last stage (buffer `last`): steps 2n-1 and 2n
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -752,27 +772,23 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // Epilogue: out = O / sum, lse = ln(sum) + reference, or (accumulate) those folded into
-  // the running result in memory.
+  // the running result read above.
+  if (!have_old) read_old();   // no stage was folded
   const float lt = xhalf_sum(lsum);
   if (!rvalid) return;
-  const size_t ridx = ((size_t)tile.b * a.hq + head) * a.nq + row;
-  __bf16* orow = static_cast<__bf16*>(a.out) + ridx * D;
-  const RowFold f = fold_row(a.acc != 0, a.acc ? a.lse[ridx] : 0.f, mref, lt);
+  const RowFold f = fold_row(a.acc != 0, lse_old, mref, lt);
+  const bool use_old = f.c_old != 0.f;   // rows with nothing folded yet (lse -inf) ignore out
 #pragma unroll
   for (int dv = 0; dv < NDV; ++dv)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      bf16x4* dst = reinterpret_cast<bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf);
       bf16x4 w;
-      if (f.c_old != 0.f) {  // rows with nothing folded yet (lse -inf) never read out
-        const bf16x4 old = *dst;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(f.c_old * (float)old[jj] + f.c_new * o[dv][4 * i + jj]);
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(o[dv][4 * i + jj] * f.c_new);
+      for (int jj = 0; jj < 4; ++jj) {
+        const float nw = f.c_new * o[dv][4 * i + jj];
+        w[jj] = (__bf16)(use_old ? __builtin_fmaf(f.c_old, (float)oldo[dv][i][jj], nw) : nw);
       }
-      *dst = w;
+      *reinterpret_cast<bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf) = w;
     }
   if (a.lse != nullptr && hf == 0) a.lse[ridx] = f.lse;
 }

@@ -132,7 +132,7 @@ int ra_rank_forward_doc(const void* q, const void* k_blocks, const void* v_block
  *
  *   out [batch, hq, nq, head_dim], dtype, device: in, the running output; out, the
  *       output over the union of its keys and this call's. Where the incoming lse is
- *       -inf the incoming out is never read (it may hold anything).
+ *       -inf the incoming out is ignored (it may hold anything, NaN included).
  *   lse [batch, hq, nq] fp32, device: in, the running lse (set it to -inf before the
  *       first call); out, the lse over the union. Must not be NULL.
  *   doc_start: NULL for no document mask, else as in ra_rank_forward_doc (then causal

@@ -6,7 +6,7 @@ sparse models?", section "How does attention survive being split?").
 Checked against the fp64 oracle's full-ring result: one launch per round in ring order,
 rounds in uneven groups, rounds in reverse order (the fold is exact in any order), with
 and without the document mask, both dtypes. The accumulator starts as lse = -inf with
-out holding NaN, which must never be read. An empty round range leaves (out, lse)
+out holding NaN, which must not reach the result. An empty round range leaves (out, lse)
 bit-identical, and one fold equals ra_merge of the accumulator with the same rounds'
 ra_rank_forward result."""
 
