@@ -15,7 +15,8 @@ from __future__ import annotations
 from . import _binding
 from ._binding import RaError, RaValueError, last_error, version  # noqa: F401
 
-__all__ = ["rank_forward", "rank_forward_doc", "rank_forward_accumulate", "merge", "version", "last_error", "RaError", "RaValueError"]
+__all__ = ["rank_forward", "rank_forward_doc", "rank_forward_accumulate", "merge", "version", "last_error",
+           "RaError", "RaValueError"]
 
 
 def _dtype_code(t):

@@ -266,7 +266,7 @@ struct Bf16Layout {
   static constexpr int ROWB = 2 * D;             // bytes per K or V row
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int TILE = BN * ROWB;         // bytes of one K (or V) tile
-  static constexpr int NB = 4;                   // stage buffers: K tiles fill LDS [0, 64K), V tiles [64K, 128K) at D = 128
+  static constexpr int NB = 4;   // stage buffers: K tiles fill LDS [0, 64K), V tiles [64K, 128K) at D = 128
   static constexpr int RPL = 128 / D;            // rows per 256-byte bank line
   static constexpr int LOADS = TILE / (16 * 64 * WAVES);  // 16-byte loads per thread per tile
   static constexpr int NKS = D / 16;             // k-steps of QK^T per 32-key sub-tile
@@ -596,7 +596,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // Q^T fragments: lane (col, hf) holds dims 16*ks + 8*hf .. +7 of its query row.
   bf16x8 qf[NKS];
   {
-    const __bf16* qrow = static_cast<const __bf16*>(a.q) + (((size_t)tile.b * a.hq + head) * a.nq + (rvalid ? row : 0)) * D;
+    const size_t qidx = ((size_t)tile.b * a.hq + head) * a.nq + (rvalid ? row : 0);
+    const __bf16* qrow = static_cast<const __bf16*>(a.q) + qidx * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * hf);
@@ -777,17 +778,20 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   const float lt = xhalf_sum(lsum);
   if (!rvalid) return;
   const RowFold f = fold_row(a.acc != 0, lse_old, mref, lt);
-  const bool use_old = f.c_old != 0.f;   // rows with nothing folded yet (lse -inf) ignore out
+  // Rows with nothing folded yet (lse -inf) ignore out: c_old is 0 there, and the old
+  // values are replaced by zeros on their bits, so a NaN cannot reach the arithmetic
+  // whatever the FP flags allow.
+  const bool use_old = f.c_old != 0.f;
 #pragma unroll
   for (int dv = 0; dv < NDV; ++dv)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const unsigned long long ob = use_old ? __builtin_bit_cast(unsigned long long, oldo[dv][i]) : 0ull;
+      const bf16x4 old = __builtin_bit_cast(bf16x4, ob);
       bf16x4 w;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float nw = f.c_new * o[dv][4 * i + jj];
-        w[jj] = (__bf16)(use_old ? __builtin_fmaf(f.c_old, (float)oldo[dv][i][jj], nw) : nw);
-      }
+      for (int jj = 0; jj < 4; ++jj)
+        w[jj] = (__bf16)__builtin_fmaf(f.c_old, (float)old[jj], f.c_new * o[dv][4 * i + jj]);
       *reinterpret_cast<bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf) = w;
     }
   if (a.lse != nullptr && hf == 0) a.lse[ridx] = f.lse;
@@ -904,7 +908,10 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
       const int c0 = 32 * dv + 8 * i + 4 * hf;
       if (c0 < d) {
         f32x4* dst = reinterpret_cast<f32x4*>(orow + c0);
-        const f32x4 old = f.c_old != 0.f ? *dst : f32x4{0.f, 0.f, 0.f, 0.f};
+        // rows with nothing folded yet (lse -inf) ignore out; the choice is made on the
+        // bits, so a NaN there cannot reach the arithmetic whatever the FP flags allow
+        const u32x4 ob = f.c_old != 0.f ? *reinterpret_cast<const u32x4*>(dst) : u32x4{0u, 0u, 0u, 0u};
+        const f32x4 old = __builtin_bit_cast(f32x4, ob);
         f32x4 w;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) w[jj] = f.c_old * old[jj] + f.c_new * o[dv][4 * i + jj];
