@@ -248,31 +248,20 @@ def balance_sweep(w, steps: int, warmup: int):
     return res
 
 
-def cpu_baseline(w, arrays, min_seconds: float = 10.0):
-    """The oracle as it stands, timed on a bounded sample of the same workload: the first
-    R query rows of batch 0 in head-major order, each as a full fp64 row against every
-    key of the c blocks. R starts at 96 and doubles until one run of the oracle takes
-    at least `min_seconds` (or covers the whole share); that run is reported."""
+def cpu_sample(w, count: int):
+    """`count` query rows of batch 0 spread evenly over the share (head-major order), so
+    light and heavy rows of a causal share enter in proportion, and the unmasked FLOP of
+    those rows (4 d per allowed key)."""
     import numpy as np
     import oracle
     from blockwise_ring_attention_amd.inputs import make_doc_start
-    q, k, v = arrays
     n = w.rows
-    ds = make_doc_start(w)
     total_rows = w.hq * n
-    count = 96
-    while True:
-        count = min(count, total_rows)
-        idx = np.arange(count)
-        rows = np.stack([np.zeros_like(idx), idx // n, idx % n], axis=1)
-        t0 = time.perf_counter()
-        oracle.rank_forward(q, k, v, w.c, w.rank, w.causal, w.zigzag, rows=rows, doc_start=ds)
-        sec = time.perf_counter() - t0
-        if sec >= min_seconds or count == total_rows:
-            break
-        count *= 2
-    # unmasked work of the sampled rows: allowed keys per row
+    count = min(count, total_rows)
+    idx = (np.arange(count, dtype=np.int64) * total_rows) // count
+    rows = np.stack([np.zeros_like(idx), idx // n, idx % n], axis=1)
     ts = rows[:, 2]
+    ds = make_doc_start(w)
     if ds is not None:
         p = oracle.chunk_positions(w.rank, n, w.c, w.zigzag)[ts]
         allowed = int(np.clip(p - np.maximum(ds[p], 0) + 1, 0, None).sum())
@@ -280,7 +269,29 @@ def cpu_baseline(w, arrays, min_seconds: float = 10.0):
         allowed = int((oracle.chunk_positions(w.rank, n, w.c, w.zigzag)[ts] + 1).sum())
     else:
         allowed = len(ts) * n * w.c
-    flop = 4 * w.head_dim * allowed
+    return rows, 4 * w.head_dim * allowed
+
+
+def cpu_baseline(w, arrays, min_seconds: float = 10.0):
+    """The oracle as it stands, timed on a bounded sample of the same workload: R query
+    rows of batch 0 spread evenly over the share, each as a full fp64 row against every
+    key of the c blocks. R starts at 96 and doubles until one run of the oracle takes at
+    least `min_seconds` (or covers the whole share); that run is reported."""
+    import oracle
+    from blockwise_ring_attention_amd.inputs import make_doc_start
+    q, k, v = arrays
+    ds = make_doc_start(w)
+    total_rows = w.hq * w.rows
+    count = 96
+    while True:
+        count = min(count, total_rows)
+        rows, flop = cpu_sample(w, count)
+        t0 = time.perf_counter()
+        oracle.rank_forward(q, k, v, w.c, w.rank, w.causal, w.zigzag, rows=rows, doc_start=ds)
+        sec = time.perf_counter() - t0
+        if sec >= min_seconds or count == total_rows:
+            break
+        count *= 2
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -297,9 +308,9 @@ def cpu_baseline(w, arrays, min_seconds: float = 10.0):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"first {count} query rows (head-major, batch 0) of {w.name}, each a full fp64 row "
-                   f"against all {w.c * n} keys (masked entries computed and discarded); {sec:.1f} s wall; "
-                   f"rate counts unmasked work only"),
+        "sample": (f"{count} query rows of batch 0 spread evenly over the share of {w.name} (head-major), each "
+                   f"a full fp64 row against all {w.c * w.rows} keys (masked entries computed and discarded); "
+                   f"{sec:.1f} s wall; rate counts unmasked work only"),
         "seconds": sec,
     }
 

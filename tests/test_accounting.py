@@ -4,6 +4,7 @@ oracle's brute-force counts and against the figures the pages print."""
 import json
 import os
 
+import numpy as np
 import pytest
 
 from blockwise_ring_attention_amd import accounting as acc
@@ -125,3 +126,28 @@ def test_binding_rejects_host_doc_start():
     k = torch.zeros(2, 1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="doc_start"):
         ra.rank_forward_doc(q, k, k, torch.zeros(8, dtype=torch.int32), 2, 0, True)
+
+
+@pytest.mark.parametrize("name", ["mha_d64_s4k_c4_zigzag_fp32", "gqa64x8_d128_s128k_c16_zigzag_bf16",
+                                  "gqa64x8_d128_s128k_c16_zigzag_docs_bf16", "tiny_c3_d8_fp32"])
+def test_cpu_sample_counts_its_rows(name):
+    """The CPU baseline's sample: rows spread over the share, and its FLOP count equal to
+    the oracle's allowed-key count of exactly those rows."""
+    import bench
+    from blockwise_ring_attention_amd.inputs import WORKLOADS, make_doc_start
+    w = WORKLOADS[name]
+    rows, flop = bench.cpu_sample(w, 96)
+    n = w.rows
+    assert len(rows) == min(96, w.hq * n) and (rows[:, 0] == 0).all()
+    assert len({tuple(r) for r in rows}) == len(rows)
+    if w.hq * n >= 192:   # both halves of a zigzag share are represented
+        assert (rows[:, 2] < n // 2).any() and (rows[:, 2] >= n // 2).any()
+    ds = make_doc_start(w)
+    if not w.causal:
+        allowed = len(rows) * n * w.c
+    else:
+        pq = A.chunk_positions(w.rank, n, w.c, w.zigzag)[rows[:, 2]]
+        pk = np.concatenate([A.chunk_positions(j, n, w.c, w.zigzag) for j in range(w.c)])
+        m = A.causal_allowed(pq, pk) if ds is None else A.document_allowed(pq, pk, ds)
+        allowed = int(m.sum())
+    assert flop == 4 * w.head_dim * allowed
