@@ -106,6 +106,17 @@ def time_workload(w, steps: int, warmup: int, arrays=None):
     return wall / steps * 1e3, sum(launch_ms) / len(launch_ms), min(launch_ms), float(np.median(launch_ms))
 
 
+def time_workload_min(w, steps: int, warmup: int, arrays=None, min_ms: float = MIN_TIMED_MS):
+    """time_workload, run again with more steps when `steps` launches last less than
+    `min_ms` (short launches are timed before the clocks settle). Returns its four
+    figures and the step count of the run reported."""
+    r = time_workload(w, steps, warmup, arrays)
+    if steps * r[0] < min_ms:
+        steps = int(np.ceil(min_ms / r[0]))
+        r = time_workload(w, steps, warmup, arrays)
+    return (*r, steps)
+
+
 def _device_inputs(w, arrays):
     import torch
     from blockwise_ring_attention_amd.inputs import make_inputs
@@ -215,7 +226,8 @@ def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumul
 def balance_sweep(w, steps: int, warmup: int):
     """Every rank r = 0..c-1 of the workload, once with contiguous chunks and once with
     the zigzag pairing (causal), each a fused launch: ms per rank and the spread. Q is the
-    same array for every rank (its values do not change the work)."""
+    same array for every rank (its values do not change the work). Each rank is timed
+    over at least MIN_TIMED_MS of launches."""
     import dataclasses
     import torch
     from blockwise_ring_attention_amd import accounting as acc
@@ -227,14 +239,14 @@ def balance_sweep(w, steps: int, warmup: int):
         ranks = []
         for r in range(w.c):
             wr = dataclasses.replace(w, rank=r, zigzag=zig)
-            ms, ml, mn, _ = time_workload(wr, steps, warmup, arrays)
+            ms, ml, mn, _, steps_r = time_workload_min(wr, steps, warmup, arrays)
             if ds is None:
                 e = acc.allowed_entries(w.c, r, w.rows, w.rows, True, zig)
             else:
                 e = acc.doc_allowed_entries(w.c, r, w.rows, zig, ds)
             flop = acc.unmasked_flop(w.batch, w.hq, w.head_dim, e)
             rec = {"rank": r, "kernel_ms": round(ml, 4), "tflops": round(flop / (ml * 1e-3) / 1e12, 1),
-                   "allowed_entries_per_head": e}
+                   "allowed_entries_per_head": e, "steps": steps_r}
             if ds is None:
                 rec["kv_blocks_with_work"] = sum(
                     1 for j in range(w.c) if acc.block_allowed(w.c, r, j, w.rows, w.rows, True, zig) > 0)
@@ -396,11 +408,7 @@ def main():
             wa = WORKLOADS[name]
             fa, _ = workload_numbers(wa)
             arrays_a = make_inputs(wa)
-            ms_a, ml_a, _, _ = time_workload(wa, args.steps, args.warmup, arrays_a)
-            steps_a = args.steps
-            if steps_a * ms_a < MIN_TIMED_MS:   # too short to time well: run again with more steps
-                steps_a = int(np.ceil(MIN_TIMED_MS / ms_a))
-                ms_a, ml_a, _, _ = time_workload(wa, steps_a, args.warmup, arrays_a)
+            ms_a, ml_a, _, _, steps_a = time_workload_min(wa, args.steps, args.warmup, arrays_a)
             del arrays_a
             also.append({"workload": name, "value": round(fa / (ms_a * 1e-3) / 1e12, 2), "ms_per_step": round(ms_a, 4),
                          "kernel_ms_avg": round(ml_a, 4), "steps": steps_a,

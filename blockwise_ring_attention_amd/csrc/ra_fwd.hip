@@ -593,9 +593,14 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   const QRange qr = tile_range(a, qlo, qhi, lane);
   const int qds = a.doc != nullptr ? a.doc[qpos] : 0;   // first key position the lane's query sees
 
-  // Q^T fragments: lane (col, hf) holds dims 16*ks + 8*hf .. +7 of its query row.
+  KvCursor<BN> lc, cc;   // next stage to load, stage being folded
+  lc.begin(a, qr);
+  cc = lc;
+
+  // Q^T fragments: lane (col, hf) holds dims 16*ks + 8*hf .. +7 of its query row. A
+  // tile with no keys to visit (in this launch's rounds) never reads them.
   bf16x8 qf[NKS];
-  {
+  if (cc.valid) {
     const size_t qidx = ((size_t)tile.b * a.hq + head) * a.nq + (rvalid ? row : 0);
     const __bf16* qrow = static_cast<const __bf16*>(a.q) + qidx * D;
 #pragma unroll
@@ -657,9 +662,6 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // stage s + NB - 2 go into its buffer during stage s. The buffers are distinct arrays and the loop is
   // unrolled over them, so the compiler can tell a stage's reads apart from the loads in
   // flight into the other buffers. Even sub-tiles use (sA, pA), odd ones (sB, pB).
-  KvCursor<BN> lc, cc;   // next stage to load, stage being folded
-  lc.begin(a, qr);
-  cc = lc;
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < NB - 2; ++s) {
@@ -677,7 +679,6 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   __bf16* const orow = static_cast<__bf16*>(a.out) + ridx * D;
   bf16x4 oldo[NDV][4] = {};
   float lse_old = kNegInf;
-  bool have_old = false;
   auto read_old = [&]() {
     if (a.acc && rvalid) {
       lse_old = a.lse[ridx];
@@ -686,9 +687,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) oldo[dv][i] = *reinterpret_cast<const bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf);
     }
-    have_old = true;
   };
 
+  const bool cc_any = cc.valid;   // some stage is folded
   if (cc.valid) {
     f32x16 sA, sB;
     bf16x8 pA[2], pB[2];
@@ -773,10 +774,15 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // Epilogue: out = O / sum, lse = ln(sum) + reference, or (accumulate) those folded into
-  // the running result read above.
-  if (!have_old) read_old();   // no stage was folded
+  // the running result read above. A tile that folded no stage has nothing to add: in
+  // accumulate mode its rows whose running lse is finite stay exactly as they are, so
+  // they are neither read nor written.
   const float lt = xhalf_sum(lsum);
   if (!rvalid) return;
+  if (a.acc && !cc_any) {
+    lse_old = a.lse[ridx];
+    if (lse_old > kNegInf) return;
+  }
   const RowFold f = fold_row(a.acc != 0, lse_old, mref, lt);
   // Rows with nothing folded yet (lse -inf) ignore out: c_old is 0 there, and the old
   // values are replaced by zeros on their bits, so a NaN cannot reach the arithmetic
