@@ -249,8 +249,9 @@ __device__ inline RowFold fold_row(bool accumulate, float lse_old, float mref, f
 // SIMD): every K/V stage staged in LDS serves 256 query columns.
 //
 // K/V stages of BN = 64 keys go straight from global memory into LDS (buffer loads that
-// write LDS), so no VGPRs are spent on staging; NB stage buffers keep up to NB - 3 stages
-// in flight behind the one being folded. Rows are 2*D bytes, unpadded; 16-byte chunks are
+// write LDS), so no VGPRs are spent on staging; of the NB stage buffers, the one being
+// folded and the previous one (whose V tile the first step still reads) are in use, and
+// the loads of the next NB - 2 stages fill the others. Rows are 2*D bytes, unpadded; 16-byte chunks are
 // XOR-swizzled per row so that both the K fragment reads (ds_read_b128, 16 rows per pass)
 // and the V^T transpose reads (ds_read_b64_tr_b16, 4 rows x 4 chunks per pass) hit
 // distinct banks.
@@ -659,9 +660,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // and 2s+1 and 2s+2 (its V). Each stage begins with a workgroup barrier, before which
   // every wave waits for its own loads of stage s: after it, stage s is complete in LDS
   // for everyone, and stage s - 2 (last read at step 2s - 2) is free, so the loads of
-  // stage s + NB - 2 go into its buffer during stage s. The buffers are distinct arrays and the loop is
-  // unrolled over them, so the compiler can tell a stage's reads apart from the loads in
-  // flight into the other buffers. Even sub-tiles use (sA, pA), odd ones (sB, pB).
+  // stage s + NB - 2 go into its buffer during stage s. The buffers are distinct arrays
+  // and the loop is unrolled over them, so the compiler can tell a stage's reads apart
+  // from the loads in flight into the other buffers. Even sub-tiles use (sA, pA), odd
+  // ones (sB, pB).
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < NB - 2; ++s) {
