@@ -306,55 +306,58 @@ struct StageLoader {
     }
   }
 
-  // kb, vb: row 0 of the slab (nkv rows of 2*D bytes; nkv * 2 * D < 2^31 is checked on
-  // the host). DOK / DOV select the K and the V tile, so a stage's loads can be spread.
-  template <bool DOK = true, bool DOV = true>
-  __device__ inline void issue(char* kst, char* vst, const __bf16* kb, const __bf16* vb, int r, int nkv) const {
-    typedef __attribute__((address_space(3))) void lds_void;
-    const int bytes = nkv * L::ROWB;
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, bytes, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, bytes, kBufferFlags);
-    const int soff = r * L::ROWB;
-    if (r + L::BN <= nkv) {
+  // The loads of one stage: buffer resources of the K and V slabs (row 0 of one (block,
+  // batch, KV head) slab: nkv rows of 2*D bytes, nkv * 2 * D < 2^31 is checked on the
+  // host) and the per-lane byte offsets of rows r .. r+BN-1. Rows past the slab's last
+  // row (only in the last, ragged tile of a block) repeat that row; the fold masks them.
+  // A plan for a stage past the end of the stream (valid = false) gets empty resources,
+  // so its loads are out of range and read nothing: every stage issues the same number
+  // of loads, and no branch is needed around them.
+  struct Plan {
+    __amdgpu_buffer_rsrc_t kr, vr;
+    int ko[L::LOADS], vo[L::LOADS];
+  };
+
+  __device__ inline Plan plan(const __bf16* kb, const __bf16* vb, int r, int nkv, bool valid) const {
+    Plan p;
+    const int bytes = valid ? nkv * L::ROWB : 0;
+    p.kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, bytes, kBufferFlags);
+    p.vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, bytes, kBufferFlags);
+    const int r0 = valid ? r : 0;
+    const int soff = r0 * L::ROWB, last = nkv - 1 - r0;
 #pragma unroll
-      for (int u = 0; u < L::LOADS; ++u) {
-        if (DOK)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kst + (u * L::WAVES + wave) * 1024), 16, koff[u],
-                                                   soff, 0, 0);
-        if (DOV)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vst + (u * L::WAVES + wave) * 1024), 16, voff[u],
-                                                   soff, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < L::LOADS; ++u) {
-        // rows past the slab repeat its last row (masked out by the fold)
-        const int back = max(0, r + row[u] - (nkv - 1)) * L::ROWB;
-        if (DOK)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kst + (u * L::WAVES + wave) * 1024), 16,
-                                                   soff + (int)koff[u] - back, 0, 0, 0);
-        if (DOV)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vst + (u * L::WAVES + wave) * 1024), 16,
-                                                   soff + (int)voff[u] - back, 0, 0, 0);
-      }
+    for (int u = 0; u < L::LOADS; ++u) {
+      const int back = max(0, row[u] - last) * L::ROWB;
+      p.ko[u] = soff + (int)koff[u] - back;
+      p.vo[u] = soff + (int)voff[u] - back;
     }
+    return p;
+  }
+
+  __device__ inline void issue_k(const Plan& p, char* kst) const {
+    typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+    for (int u = 0; u < L::LOADS; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(p.kr, (lds_void*)(kst + (u * L::WAVES + wave) * 1024), 16, p.ko[u], 0,
+                                               0, 0);
+  }
+
+  __device__ inline void issue_v(const Plan& p, char* vst) const {
+    typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+    for (int u = 0; u < L::LOADS; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(p.vr, (lds_void*)(vst + (u * L::WAVES + wave) * 1024), 16, p.vo[u], 0,
+                                               0, 0);
   }
 };
 
-// Wait until at most `stages` stages of this thread's K/V loads are still in flight
-// (loads complete in issue order). The counts are immediates, hence the branches.
-template <int D>
-__device__ __forceinline__ void wait_stages(int stages) {
-  constexpr int N = 2 * Bf16Layout<D>::LOADS;   // loads per stage per thread
-  static_assert(3 * N < 64, "vmcnt field");
-  if (stages >= 3)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | ((3 * N) & 15) | (((3 * N) >> 4) << 14));
-  else if (stages == 2)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * N) & 15) | (((2 * N) >> 4) << 14));
-  else if (stages == 1)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+// Wait until at most STAGES stages of this thread's K/V loads are still in flight (loads
+// complete in issue order; every stage issues the same number of them).
+template <int D, int STAGES>
+__device__ __forceinline__ void wait_stages() {
+  constexpr int N = STAGES * 2 * Bf16Layout<D>::LOADS;   // loads allowed in flight
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Workgroup barrier between phases. No instruction is scheduled across it, and the
@@ -651,9 +654,13 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
       vslab = vg + slab_blk * blk_stride + head_off;
     }
   };
-  auto issue = [&](char* kst, char* vst, const KvCursor<BN>& c) {
-    slab_for(c);
-    ld.issue(kst, vst, kslab, vslab, c.r, a.nkv);
+  // Plan the loads of the next stage to load (nothing, past the end of the stream) and
+  // advance the load cursor.
+  auto plan_next = [&]() {
+    slab_for(lc);
+    const typename StageLoader<D>::Plan pl = ld.plan(kslab, vslab, lc.r, a.nkv, lc.valid != 0);
+    if (lc.valid) lc.next(a, qr);
+    return pl;
   };
 
   // Stage s lives in buffer s % NB and is read by the sub-tile steps 2s-1 and 2s (its K)
@@ -663,16 +670,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // stage s + NB - 2 go into its buffer during stage s. The buffers are distinct arrays
   // and the loop is unrolled over them, so the compiler can tell a stage's reads apart
   // from the loads in flight into the other buffers. Even sub-tiles use (sA, pA), odd
-  // ones (sB, pB).
-  int issued = 0;
-#pragma unroll
-  for (int s = 0; s < NB - 2; ++s) {
-    if (lc.valid) {
-      issue(kb[s], vb[s], lc);
-      lc.next(a, qr);
-      ++issued;
-    }
-  }
+  // ones (sB, pB). Every stage issues its loads, empty ones past the end of the stream,
+  // so the wait before each barrier is the same: all but the last stage issued.
 
   // Accumulate mode: the running (out, lse) of the lane's row, read at the start of the
   // tail (Q fragments are dead by then, so the registers are free) and used by the
@@ -693,16 +692,22 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   const bool cc_any = cc.valid;   // some stage is folded
   if (cc.valid) {
+#pragma unroll
+    for (int st = 0; st < NB - 2; ++st) {
+      const typename StageLoader<D>::Plan pl = plan_next();
+      ld.issue_k(pl, kb[st]);
+      ld.issue_v(pl, vb[st]);
+    }
     f32x16 sA, sB;
     bf16x8 pA[2], pB[2];
     Frags<D> fr;   // LDS fragments in flight, read ahead across steps (see pipe_block)
     // ---- stage 0 (buffer 0): steps -1 and 0
-    wait_stages<D>(issued - 1);
+    wait_stages<D, NB - 3>();
     phase_barrier();
-    if (lc.valid) {
-      issue(kb[NB - 2], vb[NB - 2], lc);
-      lc.next(a, qr);
-      ++issued;
+    {
+      const typename StageLoader<D>::Plan pl = plan_next();
+      ld.issue_k(pl, kb[NB - 2]);
+      ld.issue_v(pl, vb[NB - 2]);
     }
     SubInfo prev = sub_info(cc, 1);
     pipe_step<D, true, false, false>(a, prev, hf, qds, qpos, sc, kb[0], vb[0], qf, koff, voff, pB, o, sA, sB, pB,
@@ -722,27 +727,19 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
           const int b = (1 + u) % NB, bp = u % NB;
           // The first V^T fragments of step 2s-1 (stage s-1's, complete since the last
           // barrier) were read at the end of step 2s-2; its K fragments wait for this one.
-          wait_stages<D>(issued - (s + 1));
+          wait_stages<D, NB - 3>();
           phase_barrier();
           // The K tile of stage s + NB - 2 is issued before step 2s-1 and its V tile before
           // step 2s: spreading a stage's loads over the stage beats issuing them in one burst.
           const int bn = (1 + u + NB - 2) % NB;
-          const bool load = lc.valid;
-          const int load_row = lc.r;
-          if (load) {
-            slab_for(lc);
-            ld.template issue<true, false>(kb[bn], vb[bn], kslab, vslab, load_row, a.nkv);
-          }
+          const typename StageLoader<D>::Plan pl = plan_next();
+          ld.issue_k(pl, kb[bn]);
           // step 2s-1: S of (s, sub 0); P.V of (s-1, sub 0); softmax of (s-1, sub 1)
           pipe_step<D, true, true, true, false, true, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf, koff,
                                                                 voff, pA, o, sA, sB, pB, mref, lsum, fr,
                                                                 kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB);
           __builtin_amdgcn_sched_barrier(0);
-          if (load) {
-            ld.template issue<false, true>(kb[bn], vb[bn], kslab, vslab, load_row, a.nkv);
-            lc.next(a, qr);
-            ++issued;
-          }
+          ld.issue_v(pl, vb[bn]);
           // step 2s: S of (s, sub 1); P.V of (s-1, sub 1); softmax of (s, sub 0)
           // ... and reads the first V^T fragments of stage s for step 2s+1 (or the tail)
           pipe_step<D, true, true, true, true, true, false, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
@@ -773,6 +770,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
                                                       koff, voff, pB, o, sB, sA, pA, mref, lsum, fr);
       }
     }
+    wait_stages<D, 0>();   // the empty loads past the end are done before the workgroup ends
   }
 
   // Epilogue: out = O / sum, lse = ln(sum) + reference, or (accumulate) those folded into
