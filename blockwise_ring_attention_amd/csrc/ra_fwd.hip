@@ -445,12 +445,17 @@ __device__ __forceinline__ void read_vt(const char* vt, const int (&voff)[D / 32
   f.vhi[slot] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * L::ROWB + voff[dv]));
 }
 
-template <int D, bool QK, bool PV, bool SM, bool PRK, bool PRV, bool NXK, bool NXV>
+struct NoExtra {
+  __device__ inline void operator()() const {}
+};
+
+// `extra` (the V loads of a stage, in its second step) is issued after product 1.
+template <int D, bool QK, bool PV, bool SM, bool PRK, bool PRV, bool NXK, bool NXV, class X = NoExtra>
 __device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const char* kn, const char* vn,
                                            const bf16x8 (&qf)[D / 16], const int (&koff)[D / 16],
                                            const int (&voff)[D / 32], const bf16x8 (&pp)[2], f32x16 (&o)[D / 32],
                                            f32x16& sn, const f32x16& sc_, float sc, float nm, f32x16& e, float& ps,
-                                           Frags<D>& f) {
+                                           Frags<D>& f, const X& extra = X()) {
   using L = Bf16Layout<D>;
   constexpr int NKS = L::NKS, NDV = L::NDV;
   static_assert(NKS == 2 * NDV, "one P.V product per QK k-step");
@@ -471,6 +476,7 @@ __device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const
   ps = 0.f;
 #pragma unroll
   for (int i = 0; i < NKS; ++i) {
+    if (i == 1) extra();
     const int j = i + AHEAD;   // the fragment read in this product's slot of the schedule
     if (j < NKS) {
       if (QK) read_k<D>(kt, koff, j, j, f);
@@ -523,19 +529,20 @@ __device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const
 // rescales O (which already holds the P.V products issued in this step, taken against
 // the old reference) and the sum, and recomputes p. Masked scores are -inf and give 0.
 template <int D, bool QK, bool PV, bool SM, bool PRK = false, bool PRV = false, bool NXK = false,
-          bool NXV = false>
+          bool NXV = false, class X = NoExtra>
 __device__ __forceinline__ void pipe_step(const FwdArgs& a, const SubInfo& si, int hf, int qds, int qpos, float sc,
                                           const char* kt, const char* vt, const bf16x8 (&qf)[D / 16],
                                           const int (&koff)[D / 16], const int (&voff)[D / 32],
                                           const bf16x8 (&pp)[2], f32x16 (&o)[D / 32], f32x16& sn, f32x16& scur,
                                           bf16x8 (&pc)[2], float& mref, float& lsum, Frags<D>& f,
-                                          const char* kn = nullptr, const char* vn = nullptr) {
+                                          const char* kn = nullptr, const char* vn = nullptr, const X& extra = X()) {
   constexpr int NDV = D / 32;
   if (SM && si.mask) mask_sub(a, si, hf, qpos, qds, scur);
   const float nm = -mref;
   f32x16 e;
   float ps;
-  pipe_block<D, QK, PV, SM, PRK, PRV, NXK, NXV>(kt, vt, kn, vn, qf, koff, voff, pp, o, sn, scur, sc, nm, e, ps, f);
+  pipe_block<D, QK, PV, SM, PRK, PRV, NXK, NXV>(kt, vt, kn, vn, qf, koff, voff, pp, o, sn, scur, sc, nm, e, ps, f,
+                                                extra);
   if (SM) {
     if (__builtin_amdgcn_ballot_w64(ps > kBig)) {
       float mx = scur[0];
@@ -738,14 +745,12 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
           pipe_step<D, true, true, true, false, true, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf, koff,
                                                                 voff, pA, o, sA, sB, pB, mref, lsum, fr,
                                                                 kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB);
-          __builtin_amdgcn_sched_barrier(0);
-          ld.issue_v(pl, vb[bn]);
           // step 2s: S of (s, sub 1); P.V of (s-1, sub 1); softmax of (s, sub 0)
           // ... and reads the first V^T fragments of stage s for step 2s+1 (or the tail)
           pipe_step<D, true, true, true, true, true, false, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
                                                                   kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB, qf,
                                                                   koff, voff, pB, o, sB, sA, pA, mref, lsum, fr,
-                                                                  nullptr, vb[b]);
+                                                                  nullptr, vb[b], [&] { ld.issue_v(pl, vb[bn]); });
           prev = sub_info(cc, 1);
           cc.next(a, qr);
           ++s;
