@@ -736,15 +736,16 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
           // barrier) were read at the end of step 2s-2; its K fragments wait for this one.
           wait_stages<D, NB - 3>();
           phase_barrier();
-          // The K tile of stage s + NB - 2 is issued before step 2s-1 and its V tile before
-          // step 2s: spreading a stage's loads over the stage beats issuing them in one burst.
+          // The K tile of stage s + NB - 2 is issued inside step 2s-1 and its V tile inside
+          // step 2s, between their MFMAs: spreading a stage's loads over the stage, away from
+          // the barrier, beats issuing them in one burst.
           const int bn = (1 + u + NB - 2) % NB;
           const typename StageLoader<D>::Plan pl = plan_next();
-          ld.issue_k(pl, kb[bn]);
           // step 2s-1: S of (s, sub 0); P.V of (s-1, sub 0); softmax of (s-1, sub 1)
           pipe_step<D, true, true, true, false, true, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf, koff,
                                                                 voff, pA, o, sA, sB, pB, mref, lsum, fr,
-                                                                kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB);
+                                                                kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB,
+                                                                [&] { ld.issue_k(pl, kb[bn]); });
           // step 2s: S of (s, sub 1); P.V of (s-1, sub 1); softmax of (s, sub 0)
           // ... and reads the first V^T fragments of stage s for step 2s+1 (or the tail)
           pipe_step<D, true, true, true, true, true, false, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
