@@ -497,7 +497,7 @@ __device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const
       for (int k = 0; k < EPS; ++k) {
         const int x = EPS * i + k;
         e[x] = fast_exp2(__builtin_fmaf(sc_[x], sc, nm));
-        ps += e[x];
+        ps = x == 0 ? e[x] : ps + e[x];
       }
     }
     if (PV && !PVFIRST) pv();
@@ -669,6 +669,12 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     if (lc.valid) lc.next(a, qr);
     return pl;
   };
+  // The same plan without a branch (the slab address is recomputed), for use inside a
+  // step; the cursor is advanced separately.
+  auto plan_at = [&](const KvCursor<BN>& c) {
+    const size_t off = (size_t)c.blk * blk_stride + head_off;
+    return ld.plan(kg + off, vg + off, c.r, a.nkv, c.valid != 0);
+  };
 
   // Stage s lives in buffer s % NB and is read by the sub-tile steps 2s-1 and 2s (its K)
   // and 2s+1 and 2s+2 (its V). Each stage begins with a workgroup barrier, before which
@@ -740,18 +746,22 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
           // step 2s, between their MFMAs: spreading a stage's loads over the stage, away from
           // the barrier, beats issuing them in one burst.
           const int bn = (1 + u + NB - 2) % NB;
-          const typename StageLoader<D>::Plan pl = plan_next();
+          typename StageLoader<D>::Plan pl;
           // step 2s-1: S of (s, sub 0); P.V of (s-1, sub 0); softmax of (s-1, sub 1)
           pipe_step<D, true, true, true, false, true, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf, koff,
                                                                 voff, pA, o, sA, sB, pB, mref, lsum, fr,
                                                                 kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB,
-                                                                [&] { ld.issue_k(pl, kb[bn]); });
+                                                                [&] {
+                                                                  pl = plan_at(lc);
+                                                                  ld.issue_k(pl, kb[bn]);
+                                                                });
           // step 2s: S of (s, sub 1); P.V of (s-1, sub 1); softmax of (s, sub 0)
           // ... and reads the first V^T fragments of stage s for step 2s+1 (or the tail)
           pipe_step<D, true, true, true, true, true, false, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
                                                                   kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB, qf,
                                                                   koff, voff, pB, o, sB, sA, pA, mref, lsum, fr,
                                                                   nullptr, vb[b], [&] { ld.issue_v(pl, vb[bn]); });
+          if (lc.valid) lc.next(a, qr);
           prev = sub_info(cc, 1);
           cc.next(a, qr);
           ++s;
