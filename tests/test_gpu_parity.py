@@ -36,6 +36,15 @@ CASES = [
     (1, 4, 2, 40, 90, 2, 1, False, False, "f32"),
     (1, 2, 2, 96, 128, 4, 3, True, True, "f32"),
     (1, 4, 1, 128, 160, 2, 0, True, True, "f32"),
+    # degenerate rings and tiny blocks
+    (1, 8, 1, 128, 128, 1, 0, True, True, "bf16"),      # c = 1: no ring, zigzag chunks 0 and 1
+    (1, 4, 2, 128, 100, 1, 0, True, False, "bf16"),     # c = 1, causal, ragged
+    (2, 2, 1, 64, 70, 1, 0, False, False, "bf16"),      # c = 1, non-causal
+    (1, 2, 1, 32, 48, 1, 0, True, True, "f32"),         # c = 1, fp32
+    (1, 8, 1, 128, 2, 4, 1, True, True, "bf16"),        # one-token zigzag chunks
+    (1, 4, 1, 128, 32, 3, 2, True, True, "bf16"),       # 16-token chunks, half a sub-tile
+    (3, 8, 1, 128, 96, 2, 0, True, True, "bf16"),       # B x Hkv = 3: no XCD grouping
+    (1, 8, 8, 128, 64, 6, 5, True, False, "bf16"),      # MHA 8 heads, last of 6 ranks, one stage
 ]
 
 
