@@ -449,7 +449,9 @@ struct NoExtra {
   __device__ inline void operator()() const {}
 };
 
-// `extra` (the V loads of a stage, in its second step) is issued after product 1.
+// `extra` is issued with product 1, inside the block: a stage's first step plans its
+// loads and issues the K tile there, its second step the V tile (branch-free, see
+// StageLoader::Plan).
 template <int D, bool QK, bool PV, bool SM, bool PRK, bool PRV, bool NXK, bool NXV, class X = NoExtra>
 __device__ __forceinline__ void pipe_block(const char* kt, const char* vt, const char* kn, const char* vn,
                                            const bf16x8 (&qf)[D / 16], const int (&koff)[D / 16],
