@@ -203,3 +203,49 @@ def test_causal_mask_regression_inputs():
         out, lse = run_gpu(q, k, v, c, rank, True, zigzag)
         ref, ref_lse = oracle.rank_forward(q, k, v, c, rank, True, zigzag)
         assert_parity(out, ref, lse, ref_lse, "bf16", "mask regression")
+
+
+@pytest.mark.parametrize("pattern", ["large", "rising", "falling"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_reference_raise_paths(pattern, dtype):
+    """Scores that keep the online softmax's reference moving: large-magnitude Q/K
+    (scaled scores in the hundreds, so the running maximum jumps far and often), keys
+    whose scores rise along the sequence (a new maximum at every sub-tile) and fall
+    along it (the first sub-tile holds the maximum). The fp64 oracle has no reference
+    at all, so any slip in the rescaling shows up here."""
+    B, hq, hkv, d, n, c, rank = 1, 4, 2, (128 if dtype == "bf16" else 64), 256, 4, 1
+    seed = 4100 + (0 if dtype == "bf16" else 7)
+    q = random_array((B, hq, n, d), dtype, seed)
+    k = random_array((c, B, hkv, n, d), dtype, seed + 1)
+    v = random_array((c, B, hkv, n, d), dtype, seed + 2)
+    if pattern == "large":
+        q = random_array((B, hq, n, d), dtype, seed, scale=6.0)
+        k = random_array((c, B, hkv, n, d), dtype, seed + 1, scale=6.0)
+    else:
+        # a common direction in every query, and keys whose component along it follows the
+        # key's global position (rising) or its negative (falling): the scaled score moves
+        # by about 10 (log2 units) per 32 keys, past the reference's slack of 8 each time
+        q = q.copy()
+        q[..., 0] += 16.0
+        pos = np.stack([oracle.chunk_positions(j, n, c, True) for j in range(c)])   # [c, n]
+        sign = 1.0 if pattern == "rising" else -1.0
+        k = k.copy()
+        k[..., 0] = (sign * 155.0 * pos / (c * n))[:, None, None, :]
+        from blockwise_ring_attention_amd.inputs import round_to_dtype
+        q, k = round_to_dtype(q, dtype), round_to_dtype(k, dtype)
+    # fp32 rounding of a score grows with the size of its terms: the fp32 bar (1e-5, for
+    # scores of order 1) is scaled by the largest |score| over 4, bf16 keeps its bar
+    kall = k.reshape(c, B, hkv, n, d).transpose(1, 2, 0, 3, 4).reshape(B, hkv, c * n, d).astype(np.float64)
+    smax = max(float(np.abs(q[0, h].astype(np.float64) @ kall[0, h // (hq // hkv)].T).max()) for h in range(hq))
+    smax /= np.sqrt(d)
+    for causal in (True, False):
+        say(f"reference raise {pattern} {dtype} causal={causal} max|score| {smax:.1f}")
+        out, lse = run_gpu(q, k, v, c, rank, causal, True, dtype=dtype)
+        ref, ref_lse = oracle.rank_forward(q, k, v, c, rank, causal, True)
+        if dtype == "bf16":
+            assert_parity(out, ref, lse, ref_lse, dtype, f"reference raise {pattern}")
+        else:
+            tol = 1e-5 * max(1.0, smax / 4.0)
+            err = np.abs(out - ref).max()
+            assert np.all(np.isfinite(out)) and err <= tol, (err, tol)
+            assert np.abs(lse - ref_lse).max() <= 1e-3
