@@ -23,6 +23,34 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(B.EXPORTED)
 
 
+def _declared_signatures():
+    """{name: [parameter type strings]} from the prototypes in include/ra.h."""
+    text = open(os.path.join(ROOT, "include", "ra.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    sigs = {}
+    for m in re.finditer(r"\b(ra_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = [p.strip() for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+        sigs[m.group(1)] = [re.sub(r"\s*\b\w+$", "", p).strip() for p in params]
+    return sigs
+
+
+def _ctype_for(c_type: str):
+    if "*" in c_type:
+        return ctypes.c_void_p
+    return {"int": ctypes.c_int, "long long": ctypes.c_longlong}[c_type]
+
+
+def test_binding_argtypes_match_the_header(ra_lib):
+    """Every ctypes prototype in the binding has the header's parameter count and types,
+    so a change on one side of the boundary cannot silently shift arguments."""
+    lib = B.load()
+    sigs = _declared_signatures()
+    assert sorted(sigs) == sorted(B.EXPORTED)
+    for name, params in sigs.items():
+        fn = getattr(lib, name)
+        assert list(fn.argtypes) == [_ctype_for(p) for p in params], name
+
+
 def test_library_exports_every_declared_symbol(ra_lib):
     for name in _declared_functions():
         assert hasattr(ra_lib, name), name
