@@ -7,9 +7,10 @@ One step = one fused launch of ra_rank_forward over the whole share (all c ring 
 causal skipping, GQA, lse) on seeded synthetic inputs already resident in HBM. The value
 is unmasked TFLOP/s: 4*d FLOP per allowed score entry over the step time. Prints one
 JSON line; it also carries the streamed form of the same share ("per_round": one launch
-per ring round, folded into the running result by the kernel's own epilogue, and the same
-with a separate ra_merge launch per round). ``--balance`` instead times every rank of the
-workload with contiguous and with zigzag chunks and prints that sweep.
+per ring round, folded into the running result by the kernel's own epilogue with the
+running out in fp32 or in bf16, and plain launches with a separate ra_merge per round).
+``--balance`` instead times every rank of the workload with contiguous and with zigzag
+chunks and prints that sweep.
 """
 
 from __future__ import annotations
@@ -153,25 +154,30 @@ def _accumulate_fn(w):
 
 def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumulate"):
     """The streamed form of the same share, as a live ring rank runs it: one launch per
-    ring round (rounds [t, t+1)), in ring order. Round 0 writes the running (out, lse) in
-    HBM; each later round is folded into it, either inside the kernel's epilogue
-    (mode "accumulate": ra_rank_forward_accumulate) or by a separate in-place ra_merge of
-    that round's partial (mode "merge"). One step = all c rounds. Returns step ms,
-    per-round kernel ms, per-merge ms (from one event-instrumented step), and the max
-    abs difference of the streamed result from the fused launch."""
+    ring round (rounds [t, t+1)), in ring order, the running (out, lse) kept in HBM.
+    Modes: "accumulate" folds every round into an fp32 running out inside the kernel's
+    epilogue (ra_rank_forward_accumulate, starting from lse = -inf) and rounds it to the
+    input dtype once at the end; "accumulate_bf16" keeps the running out in bf16 (round 0
+    a plain launch); "merge" runs plain launches and merges each later round's partial in
+    place with ra_merge. One step = all c rounds (with the fill and the final rounding).
+    Returns step ms, per-round kernel ms, per-merge ms (from one event-instrumented step),
+    and the max abs difference of the streamed result from the fused launch."""
     import torch
     import blockwise_ring_attention_amd as ra
     qd, kd, vd = _device_inputs(w, arrays)
     fwd = _forward_fn(w)
     accf = _accumulate_fn(w)
     acc = torch.empty_like(qd)
+    acc32 = torch.empty(qd.shape, dtype=torch.float32, device="cuda") if mode == "accumulate" else None
     acc_lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
     part = torch.empty_like(qd) if mode == "merge" else None
     part_lse = torch.empty_like(acc_lse) if mode == "merge" else None
     c = w.c
 
     def launch(t):
-        if t == 0:
+        if mode == "accumulate":
+            accf(qd, kd, vd, acc32, acc_lse, t, t + 1)
+        elif t == 0:
             fwd(qd, kd, vd, 0, 1, out=acc, lse=acc_lse)
         elif mode == "merge":
             fwd(qd, kd, vd, t, t + 1, out=part, lse=part_lse)
@@ -184,10 +190,14 @@ def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumul
     has_merge = mode == "merge"
 
     def step():
+        if mode == "accumulate":
+            acc_lse.fill_(float("-inf"))
         for t in range(c):
             launch(t)
             if t > 0 and has_merge:
                 merge()
+        if mode == "accumulate":
+            acc.copy_(acc32)
 
     for _ in range(warmup):
         step()
@@ -202,6 +212,8 @@ def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumul
     ms_step = e0.elapsed_time(e1) / steps
     # one instrumented step: an event pair around every launch and every merge
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(c)]
+    if mode == "accumulate":
+        acc_lse.fill_(float("-inf"))
     for t in range(c):
         ev[t][0].record(stream)
         launch(t)
@@ -210,6 +222,8 @@ def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumul
             ev[t][2].record(stream)
             merge()
             ev[t][3].record(stream)
+    if mode == "accumulate":
+        acc.copy_(acc32)
     torch.cuda.synchronize()
     round_ms = [ev[t][0].elapsed_time(ev[t][1]) for t in range(c)]
     merge_ms = [ev[t][2].elapsed_time(ev[t][3]) for t in range(1, c)] if has_merge else []
@@ -218,7 +232,7 @@ def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumul
     diff = (acc.float() - fused.float()).abs().max().item()
     fin = torch.isfinite(fused_lse)
     lse_diff = (acc_lse[fin] - fused_lse[fin]).abs().max().item() if bool(fin.any()) else 0.0
-    del qd, kd, vd, acc, acc_lse, part, part_lse, fused, fused_lse
+    del qd, kd, vd, acc, acc32, acc_lse, part, part_lse, fused, fused_lse
     torch.cuda.empty_cache()
     return ms_step, round_ms, merge_ms, diff, lse_diff
 
@@ -416,11 +430,13 @@ def main():
         line["also"] = also
     if not args.no_per_round:
         what = {"accumulate": "one ra_rank_forward_accumulate launch per ring round (rounds [t, t+1)), each "
-                              "folding its partial into the running (out, lse) in its epilogue",
+                              "folding its partial into an fp32 running (out, lse) in its epilogue; out rounded to "
+                              "bf16 once at the end",
+                "accumulate_bf16": "as accumulate with the running out kept in bf16 (round 0 a plain launch)",
                 "merge": "one ra_rank_forward launch per ring round + in-place ra_merge into the running "
                          "(out, lse)"}
         line["per_round"] = {}
-        for mode in ("accumulate", "merge"):
+        for mode in ("accumulate", "accumulate_bf16", "merge"):
             ms_pr, round_ms, merge_ms, diff, lse_diff = time_per_round(w, max(1, args.steps // 4), 1, arrays, mode)
             line["per_round"][mode] = {
                 "what": what[mode],

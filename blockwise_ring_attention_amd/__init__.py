@@ -69,11 +69,13 @@ def rank_forward_accumulate(q, k_blocks, v_blocks, out, lse, c: int, rank: int, 
                             round_begin: int = 0, round_end: int | None = None, *, doc_start=None):
     """Fold rounds [round_begin, round_end) into the running result (out, lse) in place.
 
-    ``out`` [B, Hq, Nq, d] (q's dtype) and ``lse`` [B, Hq, Nq] fp32 hold the result over
-    the keys folded so far (lse = -inf where none: start from ``lse.fill_(-inf)``; out
-    is then ignored). Afterwards they hold the result over those keys and this call's
-    rounds, which must not repeat a round already folded in. ``doc_start`` (optional)
-    adds the document mask of ``rank_forward_doc`` (causal only). Returns (out, lse).
+    ``out`` [B, Hq, Nq, d] and ``lse`` [B, Hq, Nq] fp32 hold the result over the keys
+    folded so far (lse = -inf where none: start from ``lse.fill_(-inf)``; out is then
+    ignored). Afterwards they hold the result over those keys and this call's rounds,
+    which must not repeat a round already folded in. ``out`` has q's dtype or, with
+    bf16 inputs, fp32: an fp32 running output does not gain bf16 rounding at every call.
+    ``doc_start`` (optional) adds the document mask of ``rank_forward_doc`` (causal
+    only). Returns (out, lse).
     """
     import torch
     if out is None or lse is None:
@@ -115,8 +117,10 @@ def _forward(q, k_blocks, v_blocks, doc_start, c, rank, causal, zigzag, round_be
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+    elif out.shape != q.shape or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous tensor like q")
+    elif out.dtype != q.dtype and not (accumulate and q.dtype == torch.bfloat16 and out.dtype == torch.float32):
+        raise ValueError(f"out dtype {out.dtype} does not match q's {q.dtype}")
     if lse is None and with_lse:
         lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
     elif lse is not None and (lse.shape != (B, hq, nq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
@@ -124,7 +128,8 @@ def _forward(q, k_blocks, v_blocks, doc_start, c, rank, causal, zigzag, round_be
     if accumulate:
         code = _binding.ra_rank_forward_accumulate(_ptr(q), _ptr(k_blocks), _ptr(v_blocks), _ptr(doc_start),
                                                    _ptr(out), _ptr(lse), B, hq, hkv, nq, nkv, d, c, rank, causal,
-                                                   zigzag, round_begin, round_end, dt, _stream_handle(q.device))
+                                                   zigzag, round_begin, round_end, dt, _dtype_code(out),
+                                                   _stream_handle(q.device))
         _binding.check(code, "ra_rank_forward_accumulate")
     elif doc_start is None:
         code = _binding.ra_rank_forward(_ptr(q), _ptr(k_blocks), _ptr(v_blocks), _ptr(out), _ptr(lse),

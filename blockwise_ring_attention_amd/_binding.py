@@ -47,7 +47,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.ra_rank_forward.restype = ci
     lib.ra_rank_forward_doc.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 12 + [vp]
     lib.ra_rank_forward_doc.restype = ci
-    lib.ra_rank_forward_accumulate.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 13 + [vp]
+    lib.ra_rank_forward_accumulate.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 14 + [vp]
     lib.ra_rank_forward_accumulate.restype = ci
     lib.ra_merge.argtypes = [vp, vp, vp, vp, vp, vp, cll, ci, ci, vp]
     lib.ra_merge.restype = ci
@@ -92,11 +92,11 @@ def ra_rank_forward_doc(q, k_blocks, v_blocks, doc_start, out, lse, batch, hq, h
 
 
 def ra_rank_forward_accumulate(q, k_blocks, v_blocks, doc_start, out, lse, batch, hq, hkv, nq, nkv, head_dim, c,
-                               rank, causal, zigzag, round_begin, round_end, dtype, stream) -> int:
+                               rank, causal, zigzag, round_begin, round_end, dtype, out_dtype, stream) -> int:
     """Raw call with integer pointers (doc_start 0 or None: no document mask)."""
     return load().ra_rank_forward_accumulate(q, k_blocks, v_blocks, doc_start or None, out, lse, batch, hq, hkv, nq,
                                              nkv, head_dim, c, rank, int(causal), int(zigzag), round_begin,
-                                             round_end, dtype, stream)
+                                             round_end, dtype, out_dtype, stream)
 
 
 def ra_merge(out_a, lse_a, out_b, lse_b, out, lse, rows, head_dim, dtype, stream) -> int:

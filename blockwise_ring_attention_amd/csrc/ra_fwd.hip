@@ -691,17 +691,24 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // Accumulate mode: the running (out, lse) of the lane's row, read at the start of the
   // tail (Q fragments are dead by then, so the registers are free) and used by the
   // epilogue, so the read overlaps the last P.V products instead of following them.
+  // The running out is bf16 like the inputs, or fp32 (out_f32), which keeps a long
+  // stream of folds from accumulating bf16 rounding; the fp32 one is read in the epilogue
+  // itself (its registers would not fit beside the tail's).
   const size_t ridx = ((size_t)tile.b * a.hq + head) * a.nq + row;
   __bf16* const orow = static_cast<__bf16*>(a.out) + ridx * D;
+  float* const orowf = static_cast<float*>(a.out) + ridx * D;
   bf16x4 oldo[NDV][4] = {};
   float lse_old = kNegInf;
   auto read_old = [&]() {
     if (a.acc && rvalid) {
       lse_old = a.lse[ridx];
+      if (!a.out_f32) {
 #pragma unroll
-      for (int dv = 0; dv < NDV; ++dv)
+        for (int dv = 0; dv < NDV; ++dv)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oldo[dv][i] = *reinterpret_cast<const bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf);
+          for (int i = 0; i < 4; ++i)
+            oldo[dv][i] = *reinterpret_cast<const bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf);
+      }
     }
   };
 
@@ -806,18 +813,33 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // values are replaced by zeros on their bits, so a NaN cannot reach the arithmetic
   // whatever the FP flags allow.
   const bool use_old = f.c_old != 0.f;
+  if (a.out_f32) {
 #pragma unroll
-  for (int dv = 0; dv < NDV; ++dv)
+    for (int dv = 0; dv < NDV; ++dv)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned long long ob = use_old ? __builtin_bit_cast(unsigned long long, oldo[dv][i]) : 0ull;
-      const bf16x4 old = __builtin_bit_cast(bf16x4, ob);
-      bf16x4 w;
+      for (int i = 0; i < 4; ++i) {
+        u32x4 ob = {0u, 0u, 0u, 0u};
+        if (use_old) ob = *reinterpret_cast<const u32x4*>(orowf + 32 * dv + 8 * i + 4 * hf);
+        const f32x4 old = __builtin_bit_cast(f32x4, ob);
+        f32x4 w;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        w[jj] = (__bf16)__builtin_fmaf(f.c_old, (float)old[jj], f.c_new * o[dv][4 * i + jj]);
-      *reinterpret_cast<bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf) = w;
-    }
+        for (int jj = 0; jj < 4; ++jj) w[jj] = __builtin_fmaf(f.c_old, old[jj], f.c_new * o[dv][4 * i + jj]);
+        *reinterpret_cast<f32x4*>(orowf + 32 * dv + 8 * i + 4 * hf) = w;
+      }
+  } else {
+#pragma unroll
+    for (int dv = 0; dv < NDV; ++dv)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned long long ob = use_old ? __builtin_bit_cast(unsigned long long, oldo[dv][i]) : 0ull;
+        const bf16x4 old = __builtin_bit_cast(bf16x4, ob);
+        bf16x4 w;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          w[jj] = (__bf16)__builtin_fmaf(f.c_old, (float)old[jj], f.c_new * o[dv][4 * i + jj]);
+        *reinterpret_cast<bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf) = w;
+      }
+  }
   if (a.lse != nullptr && hf == 0) a.lse[ridx] = f.lse;
 }
 

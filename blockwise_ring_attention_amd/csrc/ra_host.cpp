@@ -53,8 +53,11 @@ namespace {
 // document mask applies (then causal); `acc` folds the result into the running (out, lse).
 int forward(const void* q, const void* k_blocks, const void* v_blocks, const int* doc, void* out, float* lse,
             int batch, int hq, int hkv, int nq, int nkv, int head_dim, int c, int rank, int causal, int zigzag,
-            int round_begin, int round_end, int dtype, void* stream, bool acc = false) {
+            int round_begin, int round_end, int dtype, void* stream, bool acc = false, int out_dtype = -1) {
   if (dtype != RA_BF16 && dtype != RA_F32) return fail(RA_ERR_ARG, "unknown dtype %d", dtype);
+  if (out_dtype < 0) out_dtype = dtype;
+  if (out_dtype != dtype && !(dtype == RA_BF16 && out_dtype == RA_F32))
+    return fail(RA_ERR_ARG, "out_dtype %d not allowed with dtype %d", out_dtype, dtype);
   if (batch < 0 || nq < 0 || nkv < 0) return fail(RA_ERR_ARG, "negative size (batch=%d nq=%d nkv=%d)", batch, nq, nkv);
   if (hq < 1 || hkv < 1) return fail(RA_ERR_ARG, "hq=%d and hkv=%d must be >= 1", hq, hkv);
   if (hq % hkv != 0) return fail(RA_ERR_ARG, "hq=%d is not a multiple of hkv=%d", hq, hkv);
@@ -87,6 +90,7 @@ int forward(const void* q, const void* k_blocks, const void* v_blocks, const int
 
   ra::FwdArgs a{};
   a.q = q; a.k = k_blocks; a.v = v_blocks; a.out = out; a.lse = lse; a.doc = doc; a.acc = acc ? 1 : 0;
+  a.out_f32 = (dtype == RA_BF16 && out_dtype == RA_F32) ? 1 : 0;
   a.B = batch; a.hq = hq; a.hkv = hkv; a.nq = nq; a.nkv = nkv; a.d = head_dim;
   a.c = c; a.rank = rank; a.causal = is_causal; a.zigzag = is_zigzag; a.t0 = round_begin; a.t1 = round_end;
   const int col_blocks = dtype == RA_BF16 ? ra::kBf16ColBlocks : ra::kF32ColBlocks;
@@ -132,10 +136,12 @@ extern "C" int ra_rank_forward_doc(const void* q, const void* k_blocks, const vo
 extern "C" int ra_rank_forward_accumulate(const void* q, const void* k_blocks, const void* v_blocks,
                                           const int* doc_start, void* out, float* lse, int batch, int hq, int hkv,
                                           int nq, int nkv, int head_dim, int c, int rank, int causal, int zigzag,
-                                          int round_begin, int round_end, int dtype, void* stream) {
+                                          int round_begin, int round_end, int dtype, int out_dtype,
+                                          void* stream) {
   if (doc_start != nullptr && causal == 0) return fail(RA_ERR_ARG, "a document mask needs causal=1");
+  if (out_dtype != RA_BF16 && out_dtype != RA_F32) return fail(RA_ERR_ARG, "unknown out_dtype %d", out_dtype);
   return forward(q, k_blocks, v_blocks, doc_start, out, lse, batch, hq, hkv, nq, nkv, head_dim, c, rank, causal,
-                 zigzag, round_begin, round_end, dtype, stream, true);
+                 zigzag, round_begin, round_end, dtype, stream, true, out_dtype);
 }
 
 extern "C" int ra_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,

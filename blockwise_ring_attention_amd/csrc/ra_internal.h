@@ -14,6 +14,7 @@ struct FwdArgs {
   float* lse;           // may be null
   const int* doc;       // document starts by global position (causal document mask), or null
   int acc;              // 1: fold the result into the running (out, lse) in memory
+  int out_f32;          // 1: out is fp32 (bf16 inputs, accumulate mode), else the input type
   int B, hq, hkv, nq, nkv, d;
   int c, rank, causal, zigzag, t0, t1;
   // Work decomposition (see plan_forward in ra_host.cpp).

@@ -130,9 +130,14 @@ int ra_rank_forward_doc(const void* q, const void* k_blocks, const void* v_block
  * sparse models?", section "How does attention survive being split?"), with no separate
  * merge launch or partial buffer.
  *
- *   out [batch, hq, nq, head_dim], dtype, device: in, the running output; out, the
- *       output over the union of its keys and this call's. Where the incoming lse is
- *       -inf the incoming out is ignored (it may hold anything, NaN included).
+ *   out [batch, hq, nq, head_dim], element type out_dtype, device: in, the running
+ *       output; out, the output over the union of its keys and this call's. Where the
+ *       incoming lse is -inf the incoming out is ignored (it may hold anything, NaN
+ *       included).
+ *   out_dtype: the running output's element type: dtype, or RA_F32 with bf16 inputs.
+ *       Every call rounds the running output to its type, so a bf16 one gains up to
+ *       half a bf16 ulp per call (a few ulps over a long ring); an fp32 one keeps the
+ *       streamed result as close to the fused one as fp32 allows.
  *   lse [batch, hq, nq] fp32, device: in, the running lse (set it to -inf before the
  *       first call); out, the lse over the union. Must not be NULL.
  *   doc_start: NULL for no document mask, else as in ra_rank_forward_doc (then causal
@@ -143,15 +148,17 @@ int ra_rank_forward_doc(const void* q, const void* k_blocks, const void* v_block
  * w = e^(lse - M) for each side, out = (w_old out_old + w_new out_new) / (w_old + w_new),
  * lse = M + ln(w_old + w_new). The call's rounds must hold keys disjoint from those
  * already folded in (a ring visits each block once). Every other argument, layout and
- * error is that of ra_rank_forward, plus RA_ERR_ARG for a NULL lse or for doc_start with
- * causal = 0. An empty round range leaves (out, lse) unchanged.
+ * error is that of ra_rank_forward, plus RA_ERR_ARG for a NULL lse, for doc_start with
+ * causal = 0, or for an out_dtype other than dtype or (bf16 inputs) RA_F32. Rows to
+ * which the call's rounds contribute no key keep their (out, lse) when the running lse
+ * is finite. An empty round range leaves (out, lse) unchanged.
  */
 int ra_rank_forward_accumulate(const void* q, const void* k_blocks, const void* v_blocks,
                                const int* doc_start, void* out, float* lse,
                                int batch, int hq, int hkv, int nq, int nkv, int head_dim,
                                int c, int rank, int causal, int zigzag,
                                int round_begin, int round_end,
-                               int dtype, void* stream);
+                               int dtype, int out_dtype, void* stream);
 
 /*
  * ra_merge -- combine two partial results over disjoint key sets into the result over

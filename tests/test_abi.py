@@ -133,11 +133,12 @@ def test_forward_doc_empty_is_a_noop(ra_lib):
 
 def _fwd_acc(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, doc=0, out=FAKE, lse=FAKE, batch=1, hq=4, hkv=2, nq=64, nkv=64, d=128, c=4,
-             rank=1, causal=1, zigzag=1, t0=0, t1=4, dtype=B.RA_BF16)
+             rank=1, causal=1, zigzag=1, t0=0, t1=4, dtype=B.RA_BF16, out_dtype=None)
     a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
     return B.ra_rank_forward_accumulate(a["q"], a["k"], a["v"], a["doc"], a["out"], a["lse"], a["batch"], a["hq"],
                                         a["hkv"], a["nq"], a["nkv"], a["d"], a["c"], a["rank"], a["causal"],
-                                        a["zigzag"], a["t0"], a["t1"], a["dtype"], None)
+                                        a["zigzag"], a["t0"], a["t1"], a["dtype"], od, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -150,6 +151,9 @@ def _fwd_acc(**kw):
     (dict(nkv=32), B.RA_ERR_SHAPE),
     (dict(d=96), B.RA_ERR_UNSUPPORTED),
     (dict(out=0), B.RA_ERR_ARG),
+    (dict(out_dtype=7), B.RA_ERR_ARG),
+    (dict(dtype=B.RA_F32, d=64, out_dtype=B.RA_BF16), B.RA_ERR_ARG),   # fp32 inputs need an fp32 out
+    (dict(out_dtype=B.RA_F32, out=FAKE + 8), B.RA_ERR_ALIGN),
 ])
 def test_forward_accumulate_argument_errors(ra_lib, kw, code):
     assert _fwd_acc(**kw) == code

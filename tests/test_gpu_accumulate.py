@@ -54,9 +54,9 @@ def _device(q, k, v, ds, dtype):
     return to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), dd
 
 
-def _fresh_accumulator(qd):
+def _fresh_accumulator(qd, out_f32=False):
     import torch
-    out = torch.full_like(qd, float("nan"))
+    out = torch.full(qd.shape, float("nan"), dtype=torch.float32 if out_f32 else qd.dtype, device=qd.device)
     lse = torch.full(qd.shape[:3], float("-inf"), dtype=torch.float32, device=qd.device)
     return out, lse
 
@@ -67,15 +67,19 @@ def _host(out, lse):
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
+# bf16 inputs run with a bf16 and with an fp32 running output; fp32 inputs have only fp32
+CASES_OUT = [case + (False,) for case in CASES] + [case + (True,) for case in CASES if case[9] == "bf16"]
+
+
 @pytest.mark.parametrize("grouping", sorted(GROUPINGS))
-@pytest.mark.parametrize("B,hq,hkv,d,n,c,rank,causal,zigzag,dtype,doc", CASES)
-def test_streamed_ring_parity(B, hq, hkv, d, n, c, rank, causal, zigzag, dtype, doc, grouping):
+@pytest.mark.parametrize("B,hq,hkv,d,n,c,rank,causal,zigzag,dtype,doc,out32", CASES_OUT)
+def test_streamed_ring_parity(B, hq, hkv, d, n, c, rank, causal, zigzag, dtype, doc, out32, grouping):
     import blockwise_ring_attention_amd as ra
     say(f"accumulate {grouping} B={B} hq={hq} hkv={hkv} d={d} n={n} c={c} rank={rank} causal={causal} "
-        f"zigzag={zigzag} {dtype} doc={doc}")
+        f"zigzag={zigzag} {dtype} doc={doc} out32={out32}")
     q, k, v, ds = _inputs(B, hq, hkv, d, n, c, dtype, doc, 1300 + n + c + rank)
     qd, kd, vd, dd = _device(q, k, v, ds, dtype)
-    out, lse = _fresh_accumulator(qd)
+    out, lse = _fresh_accumulator(qd, out32)
     for t0, t1 in GROUPINGS[grouping](c):
         ra.rank_forward_accumulate(qd, kd, vd, out, lse, c, rank, causal, zigzag, t0, t1, doc_start=dd)
     o, l = _host(out, lse)
@@ -122,7 +126,8 @@ def test_fold_equals_merge_of_partials(dtype):
     assert torch.allclose(lse, m_lse, rtol=0, atol=1e-5)
 
 
-def test_streamed_ring_full_size_32k():
+@pytest.mark.parametrize("out32", [False, True])
+def test_streamed_ring_full_size_32k(out32):
     """The 32k GQA share (c = 8, rank 3, zigzag) streamed round by round at full size:
     equal to the fused launch within the bf16 bar, and sampled rows equal to the oracle."""
     import torch
@@ -133,7 +138,7 @@ def test_streamed_ring_full_size_32k():
     q, k, v = make_inputs(w)
     qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
     fused, fused_lse = ra.rank_forward(qd, kd, vd, w.c, w.rank, w.causal, w.zigzag)
-    out, lse = _fresh_accumulator(qd)
+    out, lse = _fresh_accumulator(qd, out32)
     for t in range(w.c):
         ra.rank_forward_accumulate(qd, kd, vd, out, lse, w.c, w.rank, w.causal, w.zigzag, t, t + 1)
     torch.cuda.synchronize()
