@@ -175,6 +175,9 @@ int ra_rank_forward_accumulate(const void* q, const void* k_blocks, const void* 
  *   out_a, out_b, out   [rows, head_dim], element type = dtype (fp32 arithmetic)
  *   lse_a, lse_b, lse   [rows] fp32
  * out may alias out_a or out_b and lse may alias lse_a or lse_b (in-place update).
+ * Each merge rounds out to dtype: a long stream of in-place bf16 merges gains up to half
+ * a bf16 ulp per merge, which ra_rank_forward_accumulate with an fp32 running output
+ * avoids.
  * rows = 0 enqueues nothing and returns RA_OK.
  * Errors: RA_ERR_ARG (null pointer, rows < 0, unknown dtype), RA_ERR_UNSUPPORTED
  * (head_dim not a multiple of 8 in [8, 512]), RA_ERR_ALIGN, RA_ERR_LAUNCH.
