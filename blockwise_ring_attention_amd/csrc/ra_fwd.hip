@@ -692,22 +692,30 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // tail (Q fragments are dead by then, so the registers are free) and used by the
   // epilogue, so the read overlaps the last P.V products instead of following them.
   // The running out is bf16 like the inputs, or fp32 (out_f32), which keeps a long
-  // stream of folds from accumulating bf16 rounding; the fp32 one is read in the epilogue
-  // itself (its registers would not fit beside the tail's).
+  // stream of folds from accumulating bf16 rounding. `oldr` holds the lane's old elements
+  // as raw bits: four fp32 words, or four bf16 values in the low two words.
   const size_t ridx = ((size_t)tile.b * a.hq + head) * a.nq + row;
   __bf16* const orow = static_cast<__bf16*>(a.out) + ridx * D;
   float* const orowf = static_cast<float*>(a.out) + ridx * D;
-  bf16x4 oldo[NDV][4] = {};
+  u32x4 oldr[NDV][4] = {};
   float lse_old = kNegInf;
   auto read_old = [&]() {
     if (a.acc && rvalid) {
       lse_old = a.lse[ridx];
-      if (!a.out_f32) {
+      if (a.out_f32) {
 #pragma unroll
         for (int dv = 0; dv < NDV; ++dv)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            oldo[dv][i] = *reinterpret_cast<const bf16x4*>(orow + 32 * dv + 8 * i + 4 * hf);
+          for (int i = 0; i < 4; ++i) oldr[dv][i] = *reinterpret_cast<const u32x4*>(orowf + 32 * dv + 8 * i + 4 * hf);
+      } else {
+#pragma unroll
+        for (int dv = 0; dv < NDV; ++dv)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 b = *reinterpret_cast<const u32x2*>(orow + 32 * dv + 8 * i + 4 * hf);
+            oldr[dv][i] = u32x4{b[0], b[1], 0u, 0u};
+          }
       }
     }
   };
@@ -818,8 +826,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     for (int dv = 0; dv < NDV; ++dv)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        u32x4 ob = {0u, 0u, 0u, 0u};
-        if (use_old) ob = *reinterpret_cast<const u32x4*>(orowf + 32 * dv + 8 * i + 4 * hf);
+        const u32x4 ob = use_old ? oldr[dv][i] : u32x4{0u, 0u, 0u, 0u};
         const f32x4 old = __builtin_bit_cast(f32x4, ob);
         f32x4 w;
 #pragma unroll
@@ -831,7 +838,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     for (int dv = 0; dv < NDV; ++dv)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const unsigned long long ob = use_old ? __builtin_bit_cast(unsigned long long, oldo[dv][i]) : 0ull;
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 ob = use_old ? u32x2{oldr[dv][i][0], oldr[dv][i][1]} : u32x2{0u, 0u};
         const bf16x4 old = __builtin_bit_cast(bf16x4, ob);
         bf16x4 w;
 #pragma unroll
