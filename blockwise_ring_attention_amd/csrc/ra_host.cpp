@@ -45,7 +45,7 @@ int heads_per_workgroup(int G, int col_blocks) {
 
 extern "C" const char* ra_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int ra_version(void) { return 200; }  // 0.2.0
+extern "C" int ra_version(void) { return 300; }  // 0.3.0
 
 namespace {
 

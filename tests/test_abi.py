@@ -58,7 +58,7 @@ def test_library_exports_every_declared_symbol(ra_lib):
 
 
 def test_version(ra_lib):
-    assert B.version() == 200
+    assert B.version() == 300
 
 
 FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced (every call below fails its checks)
