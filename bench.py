@@ -361,7 +361,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one rank's share on one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library computes one rank's share; the ring's transfers between GPUs are not part of it)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
