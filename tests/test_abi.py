@@ -205,3 +205,23 @@ def test_check_raises_with_text(ra_lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         B.load(str(tmp_path / "libra.so"))
+
+
+def test_sweep_configurations_are_valid():
+    """Every configuration of the GPU sweep passes the library's own argument rules, and
+    the sweep spans the modes and flags it claims to."""
+    from tests.test_gpu_sweep import N_CASES, _draw
+    modes, flags = set(), set()
+    for i in range(N_CASES):
+        p = _draw(i)
+        assert p["hq"] % p["hkv"] == 0 and 1 <= p["hq"] <= 32
+        assert (p["dtype"] == "bf16" and p["d"] in (64, 128)) or (p["dtype"] == "f32" and p["d"] % 8 == 0
+                                                                  and 8 <= p["d"] <= 128)
+        assert 0 <= p["rank"] < p["c"] and 0 <= p["t0"] <= p["t1"] <= p["c"]
+        assert p["n"] >= 2 and (not p["zigzag"] or p["n"] % 2 == 0)
+        assert p["mode"] != "doc" or p["causal"]
+        assert p["mode"] != "accumulate" or p["t1"] > p["t0"]
+        modes.add(p["mode"])
+        flags.add((p["causal"], p["zigzag"], p["dtype"]))
+    assert modes == {"fused", "doc", "accumulate"}
+    assert len(flags) >= 7
