@@ -347,10 +347,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle's CPU rate")
+    ap.add_argument("--no-also", action="store_true", help="skip the other workloads timed beside the main one")
     ap.add_argument("--no-per-round", action="store_true",
-                    help="skip the streamed form (one launch per ring round plus ra_merge)")
+                    help="skip the streamed form (one launch per ring round folding into a running "
+                         "(out, lse), with an fp32 or bf16 running out, or plain launches plus ra_merge)")
     ap.add_argument("--balance", action="store_true",
                     help="only run the all-rank sweep (contiguous vs zigzag chunks) of the workload and print it")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
