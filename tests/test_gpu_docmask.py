@@ -8,7 +8,9 @@ documents crossing chunk and tile edges), a single document (the causal mask), e
 token its own document, start values that are not monotone, and start values past the
 query (rows without keys); both dtypes, zigzag and contiguous ownership, round ranges.
 The 128k packed-document workload is checked on sampled rows and, over every row, by
-the Q = 0 closed form (uniform weights over the document prefix)."""
+the Q = 0 closed form (uniform weights over the document prefix); its streamed form (one
+accumulating launch per round) on sampled rows and, over every row, against the fused
+launch's lse."""
 
 import numpy as np
 import pytest
@@ -153,3 +155,42 @@ def test_docs_fullsize_zero_queries(docs_workload):
             cnt += e.size
     say(f"{w.name}: Q=0 max abs {worst:.2e} mean abs {total / cnt:.2e}")
     assert worst <= 2e-2 and total / cnt <= 2e-3
+
+
+def test_docs_fullsize_streamed_sampled_rows(docs_workload):
+    """The packed-document share streamed round by round (one ra_rank_forward_accumulate
+    launch per ring round with the document mask, into an fp32 running output that starts
+    at lse = -inf over NaN), rounded to bf16 at the end: sampled rows against the oracle
+    and, over every row, the lse of the fused launch."""
+    import torch
+    import blockwise_ring_attention_amd as ra
+    w, (q, k, v), ds = docs_workload
+    n = w.rows
+    say(f"{w.name}: streamed ring with documents, {w.c} launches")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    dd = torch.from_numpy(np.ascontiguousarray(ds, dtype=np.int32)).cuda()
+    out = torch.full(qd.shape, float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full(qd.shape[:3], float("-inf"), dtype=torch.float32, device="cuda")
+    for t in range(w.c):
+        ra.rank_forward_accumulate(qd, kd, vd, out, lse, w.c, w.rank, True, w.zigzag, t, t + 1, doc_start=dd)
+    fused_out, fused_lse = ra.rank_forward_doc(qd, kd, vd, dd, w.c, w.rank, w.zigzag)
+    torch.cuda.synchronize()
+    o = out.to(torch.bfloat16).float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    fl = fused_lse.cpu().numpy().astype(np.float64)
+    del qd, kd, vd, dd, out, lse, fused_out, fused_lse
+    torch.cuda.empty_cache()
+    assert np.array_equal(np.isneginf(l), np.isneginf(fl))
+    fin = ~np.isneginf(fl)
+    assert np.abs(l[fin] - fl[fin]).max() <= 1e-3
+    rng = np.random.default_rng(6)
+    pos = oracle.chunk_positions(w.rank, n, w.c, w.zigzag)
+    starts = np.nonzero(ds[pos] == pos)[0]
+    ts = np.unique(np.concatenate([starts[:10], [0, n // 2 - 1, n // 2, n - 1], rng.integers(0, n, 40)]))
+    rows = np.array([(0, h, t) for h in (0, 9, 63) for t in ts], dtype=np.int64)
+    say(f"{w.name}: oracle on {len(rows)} rows")
+    ref, ref_lse = oracle.rank_forward(q, k, v, w.c, w.rank, True, w.zigzag, rows=rows, doc_start=ds)
+    got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    got_lse = l[rows[:, 0], rows[:, 1], rows[:, 2]]
+    mx, mean = assert_parity(got, ref, got_lse, ref_lse, "bf16", f"{w.name} streamed")
+    say(f"{w.name}: streamed max abs {mx:.2e} mean abs {mean:.2e}")
