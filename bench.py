@@ -37,6 +37,118 @@ KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_ring_attention_amd", "csrc", f)
                   for f in ("ra_fwd.hip", "ra_internal.h")]
 
 
+XGMI_LINK_GBPS = 153.0         # one MI355X xGMI link, one direction (spec figure)
+PAGES_H100_TFLOPS = 989.0     # the pages' break-even arithmetic: H100 dense bf16 ...
+PAGES_NVLINK_GBPS = 450.0     # ... over NVLink
+
+
+class ClockSampler:
+    """Polls the GPU's graphics clock (and socket power) through amdsmi's gpu_metrics
+    while the timed launches run, from a daemon thread every `period_s`. The device is
+    matched to torch's by PCI address. Any failure leaves the result with an "error"
+    entry instead of figures: the clock is reported, never required."""
+
+    def __init__(self, device_index: int = 0, period_s: float = 0.02):
+        self.device_index = device_index
+        self.period_s = period_s
+        self.samples, self.xcd, self.power = [], [], []
+        self.error = None
+        self._handle = None
+        self._stop = None
+        self._thread = None
+
+    def _open(self):
+        import amdsmi
+        import torch
+        amdsmi.amdsmi_init()
+        props = torch.cuda.get_device_properties(self.device_index)
+        want = (int(props.pci_domain_id), int(props.pci_bus_id), int(props.pci_device_id))
+        handles = amdsmi.amdsmi_get_processor_handles()
+        for h in handles:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "DDDD:BB:DD.F"
+            dom, bus, rest = bdf.split(":")
+            if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                return h
+        if len(handles) == 1:
+            return handles[0]
+        raise RuntimeError(f"no amdsmi device at PCI {want} among {len(handles)}")
+
+    def _read(self):
+        import amdsmi
+        m = amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = m.get("current_gfxclks")
+        xcd = [int(x) for x in clks if isinstance(x, (int, float)) and 0 < x < 10000] if isinstance(clks, list) else []
+        one = m.get("current_gfxclk")
+        if not isinstance(one, (int, float)) or not 0 < one < 10000:
+            one = sum(xcd) / len(xcd) if xcd else None
+        pw = m.get("current_socket_power")
+        if not isinstance(pw, (int, float)) or not 0 < pw < 100000:
+            pw = m.get("average_socket_power")
+        return one, xcd, pw if isinstance(pw, (int, float)) and 0 < pw < 100000 else None
+
+    def __enter__(self):
+        import threading
+        try:
+            self._handle = self._open()
+            self._read()
+        except Exception as e:   # noqa: BLE001 - report, never fail the bench
+            self.error = f"{type(e).__name__}: {e}"
+            return self
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    one, xcd, pw = self._read()
+                    if one is not None:
+                        self.samples.append(one)
+                    if xcd:
+                        self.xcd.append(xcd)
+                    if pw is not None:
+                        self.power.append(pw)
+                except Exception as e:   # noqa: BLE001
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                self._stop.wait(self.period_s)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def result(self):
+        if not self.samples:
+            return {"error": self.error or "no samples"}
+        r = {"gfx_mhz_mean": round(float(np.mean(self.samples)), 1), "gfx_mhz_min": float(np.min(self.samples)),
+             "gfx_mhz_max": float(np.max(self.samples)), "samples": len(self.samples),
+             "source": f"amdsmi gpu_metrics current_gfxclk, polled every {self.period_s * 1e3:.0f} ms "
+                       "during the timed launches"}
+        if self.xcd:
+            width = min(len(x) for x in self.xcd)
+            r["per_xcd_mhz_mean"] = [round(float(np.mean([x[i] for x in self.xcd])), 1) for i in range(width)]
+        if self.power:
+            r["socket_power_w_mean"] = round(float(np.mean(self.power)), 1)
+        if self.error:
+            r["error"] = self.error
+        return r
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def kernel_sha() -> str:
     """sha256[:16] over the forward kernel's sources (the kernel file, then its header)."""
     h = hashlib.sha256()
@@ -76,7 +188,7 @@ def workload_numbers(w):
     return flop, nbytes
 
 
-def time_workload(w, steps: int, warmup: int, arrays=None):
+def time_workload(w, steps: int, warmup: int, arrays=None, clock=None):
     import torch
     import blockwise_ring_attention_amd as ra
     qd, kd, vd = _device_inputs(w, arrays)
@@ -94,6 +206,8 @@ def time_workload(w, steps: int, warmup: int, arrays=None):
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
+    if clock is not None:
+        clock.__enter__()
     t0 = time.perf_counter()
     for e0, e1 in ev:
         e0.record(stream)
@@ -101,6 +215,8 @@ def time_workload(w, steps: int, warmup: int, arrays=None):
         e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if clock is not None:
+        clock.__exit__(None, None, None)
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     del qd, kd, vd, out, lse
     torch.cuda.empty_cache()
@@ -274,6 +390,37 @@ def balance_sweep(w, steps: int, warmup: int):
     return res
 
 
+def break_even_context(w, kernel_ms: float, tflops: float):
+    """The pages' compute/transfer break-even, quoted as hardware arithmetic (not a
+    measured result or a target), beside the same arithmetic for this workload at the
+    measured rate ("What do you do about long sequences and sparse models?", section
+    "When is the ring actually free?": a block of c tokens costs 4 d c^2 FLOP against
+    4 c d bytes to send, so the send hides when c >= F / B)."""
+    eb = 2 if w.dtype == "bf16" else 4
+    block_bytes = 2 * w.batch * w.hkv * w.rows * w.head_dim * eb        # one K and V block
+    round_ms = kernel_ms / w.c                                          # mean ring round of the fused launch
+    ctx = {
+        "pages_break_even_tokens": round(PAGES_H100_TFLOPS * 1e12 / (PAGES_NVLINK_GBPS * 1e9), 1),
+        "pages_arithmetic": f"{PAGES_H100_TFLOPS:.0f} TFLOP/s (H100) / {PAGES_NVLINK_GBPS:.0f} GB/s (NVLink) "
+                            "= tokens per block at which a block's compute hides its transfer (single head)",
+        "same_arithmetic_mi355x_one_xgmi_link_tokens": round(tflops * 1e12 / (XGMI_LINK_GBPS * 1e9), 1),
+        "mean_round_ms": round(round_ms, 4),
+        "kv_block_bytes": block_bytes,
+        "link_gbps_needed_to_hide_a_round": round(block_bytes / (round_ms * 1e-3) / 1e9, 1),
+        "xgmi_link_gbps": XGMI_LINK_GBPS,
+    }
+    if w.causal and w.zigzag and w.c > 1:
+        # a non-local zigzag round holds 2 m^2 of the share's (2c-1) m^2 + m(m+1) entries
+        m = w.rows // 2
+        frac = 2 * m * m / ((2 * w.c - 1) * m * m + m * (m + 1))
+        ctx["nonlocal_round_ms_at_measured_rate"] = round(kernel_ms * frac, 4)
+        ctx["link_gbps_needed_nonlocal_round"] = round(block_bytes / (kernel_ms * frac * 1e-3) / 1e9, 1)
+        # m >= F Hkv / (B Hq): the zigzag GQA form of the same inequality
+        ctx["min_chunk_tokens_to_hide_on_one_link"] = round(
+            tflops * 1e12 * w.hkv / (XGMI_LINK_GBPS * 1e9 * w.hq), 1)
+    return ctx
+
+
 def cpu_sample(w, count: int):
     """`count` query rows of batch 0 spread evenly over the share (head-major order), so
     light and heavy rows of a causal share enter in proportion, and the unmasked FLOP of
@@ -333,6 +480,7 @@ def cpu_baseline(w, arrays, min_seconds: float = 10.0):
         "value": flop / sec / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{count} query rows of batch 0 spread evenly over the share of {w.name} (head-major), each "
                    f"a full fp64 row against all {w.c * w.rows} keys (masked entries computed and discarded); "
@@ -390,7 +538,8 @@ def main():
         return
     flop, nbytes = workload_numbers(w)
     arrays = make_inputs(w)
-    ms_step, ms_launch, ms_min, ms_med = time_workload(w, args.steps, args.warmup, arrays)
+    clock = ClockSampler()
+    ms_step, ms_launch, ms_min, ms_med = time_workload(w, args.steps, args.warmup, arrays, clock=clock)
     value = flop / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flop / (ms_launch * 1e-3) / 1e12
@@ -418,6 +567,13 @@ def main():
                      "algorithmic_bytes": nbytes, "kernel_ms_avg": round(ms_launch, 4),
                      "kernel_ms_min": round(ms_min, 4), "kernel_ms_median": round(ms_med, 4)},
     }
+    clk = clock.result()
+    if "gfx_mhz_mean" in clk:
+        # the nominal peak assumes 2.4 GHz; at the clock held under this load it is lower
+        clk["peak_at_observed_clock_tflops"] = round(peak * clk["gfx_mhz_mean"] / 2400.0, 1)
+        clk["frac_of_peak_at_observed_clock"] = round(achieved / clk["peak_at_observed_clock_tflops"], 4)
+    line["clock"] = clk
+    line["context"] = break_even_context(w, ms_launch, achieved)
     if not args.no_also:
         also = []
         for name in ALSO_WORKLOADS:

@@ -90,8 +90,9 @@ def rank_forward_accumulate(q, k_blocks, v_blocks, out, lse, c: int, rank: int, 
 
 def _check_doc(doc_start, c, k_blocks):
     import torch
-    if not doc_start.is_cuda or doc_start.dtype != torch.int32 or not doc_start.is_contiguous():
-        raise ValueError("doc_start must be a contiguous int32 GPU tensor")
+    if (not doc_start.is_cuda or doc_start.dtype != torch.int32 or not doc_start.is_contiguous()
+            or doc_start.device != k_blocks.device):
+        raise ValueError("doc_start must be a contiguous int32 GPU tensor on the inputs' device")
     if doc_start.dim() != 1 or doc_start.numel() != c * k_blocks.shape[3]:
         raise ValueError(f"doc_start needs c * n = {c * k_blocks.shape[3]} entries, got {tuple(doc_start.shape)}")
 
@@ -102,8 +103,8 @@ def _forward(q, k_blocks, v_blocks, doc_start, c, rank, causal, zigzag, round_be
     if round_end is None:
         round_end = c
     for name, t in (("q", q), ("k_blocks", k_blocks), ("v_blocks", v_blocks)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a GPU tensor on q's device")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         if t.dtype != q.dtype:
@@ -123,8 +124,9 @@ def _forward(q, k_blocks, v_blocks, doc_start, c, rank, causal, zigzag, round_be
         raise ValueError(f"out dtype {out.dtype} does not match q's {q.dtype}")
     if lse is None and with_lse:
         lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
-    elif lse is not None and (lse.shape != (B, hq, nq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, Nq]")
+    elif lse is not None and (lse.shape != (B, hq, nq) or lse.dtype != torch.float32 or not lse.is_contiguous()
+                              or lse.device != q.device):
+        raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, Nq] on q's device")
     if accumulate:
         code = _binding.ra_rank_forward_accumulate(_ptr(q), _ptr(k_blocks), _ptr(v_blocks), _ptr(doc_start),
                                                    _ptr(out), _ptr(lse), B, hq, hkv, nq, nkv, d, c, rank, causal,
@@ -151,15 +153,21 @@ def merge(out_a, lse_a, out_b, lse_b, *, out=None, lse=None):
     if out_a.shape != out_b.shape or lse_a.shape != lse_b.shape or out_a.shape[:-1] != lse_a.shape:
         raise ValueError("merge needs out_a/out_b [..., d] and lse_a/lse_b [...] of matching shapes")
     for t in (out_a, lse_a, out_b, lse_b):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("merge inputs must be contiguous GPU tensors")
+        if not t.is_cuda or not t.is_contiguous() or t.device != out_a.device:
+            raise ValueError("merge inputs must be contiguous GPU tensors on one device")
     if lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32 or out_b.dtype != out_a.dtype:
         raise ValueError("lse must be fp32 and both outputs share a dtype")
     dt = _dtype_code(out_a)
     if out is None:
         out = torch.empty_like(out_a)
+    elif (out.shape != out_a.shape or out.dtype != out_a.dtype or not out.is_contiguous()
+          or out.device != out_a.device):
+        raise ValueError("out must be a contiguous tensor of out_a's shape, dtype and device")
     if lse is None:
         lse = torch.empty_like(lse_a)
+    elif (lse.shape != lse_a.shape or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or lse.device != out_a.device):
+        raise ValueError("lse must be a contiguous fp32 tensor of lse_a's shape on out_a's device")
     rows = lse_a.numel()
     code = _binding.ra_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out), _ptr(lse), rows,
                              out_a.shape[-1], dt, _stream_handle(out_a.device))

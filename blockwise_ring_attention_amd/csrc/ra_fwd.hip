@@ -172,6 +172,13 @@ struct KvCursor {
   }
 };
 
+// Document start of the query at global position p, clamped to [0, c*nkv]: every key
+// position x lies in [0, c*nkv), so x >= start keeps its meaning, and differences with
+// positions (KvCursor::enter) cannot overflow int32 whatever the caller stored.
+__device__ inline int doc_start_at(const FwdArgs& a, int p) {
+  return min(max(a.doc[p], 0), a.c * a.nkv);
+}
+
 // The tile's QRange: positions qlo..qhi are contiguous (a tile never straddles a zigzag
 // chunk). Under the document mask every wave reduces doc_start over those positions
 // (at most 4 loads per lane, once per workgroup); the reduction is wave-uniform.
@@ -180,7 +187,7 @@ __device__ inline QRange tile_range(const FwdArgs& a, int qlo, int qhi, int lane
   if (a.doc != nullptr) {
     int mn = 0x7fffffff, mx = -0x7fffffff - 1;
     for (int p = qlo + lane; p <= qhi; p += 64) {
-      const int v = a.doc[p];
+      const int v = doc_start_at(a, p);
       mn = min(mn, v);
       mx = max(mx, v);
     }
@@ -604,7 +611,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int qlo = a.causal ? query_pos(a, tile.row0) : 0;
   const int qhi = a.causal ? query_pos(a, tile.row_end - 1) : 0;
   const QRange qr = tile_range(a, qlo, qhi, lane);
-  const int qds = a.doc != nullptr ? a.doc[qpos] : 0;   // first key position the lane's query sees
+  const int qds = a.doc != nullptr ? doc_start_at(a, qpos) : 0;   // first key position the lane's query sees
 
   KvCursor<BN> lc, cc;   // next stage to load, stage being folded
   lc.begin(a, qr);
@@ -880,7 +887,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   const int qlo = a.causal ? query_pos(a, tile.row0) : 0;
   const int qhi = a.causal ? query_pos(a, tile.row_end - 1) : 0;
   const QRange qr = tile_range(a, qlo, qhi, lane);
-  const int qds = a.doc != nullptr ? a.doc[qpos] : 0;
+  const int qds = a.doc != nullptr ? doc_start_at(a, qpos) : 0;
 
   float qf[DP / 2];
   const float* qrow = qg + (((size_t)tile.b * a.hq + head) * a.nq + (rvalid ? row : 0)) * d;

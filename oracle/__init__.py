@@ -9,7 +9,7 @@ Functions and their pins (the tests that tie each one to something other than it
 
 * ``attention.rank_forward`` -- full-row softmax attention, the definition the ring
   reaches exactly. Pinned by: 50-digit brute force on tiny inputs; the independent
-  blockwise fold in any block order; torch's fp64 scaled-dot-product attention with
+  blockwise combination of per-block partials in any block order; torch's fp64 scaled-dot-product attention with
   ``enable_gqa`` on the full sequence; gathering rank rows out of full-sequence causal
   attention; closed forms (Q = 0, constant V, key shift).
 * ``attention.rank_forward(..., doc_start=...)`` -- the document mask of packed
@@ -18,9 +18,10 @@ Functions and their pins (the tests that tie each one to something other than it
   out of the full sequence; the Q = 0 closed form (lse = ln of the document prefix).
 * ``attention.merge`` -- combination of two partial results. Pinned by: merging results
   over disjoint key sets equals the oracle over their union; identity and symmetry.
-* ``fold.online_softmax_fold`` -- the online-softmax update, a second implementation
-  used only to pin the first. Pinned by: the same brute force, and equality with the
-  full row in every order.
+* ``fold.blockwise_attention`` -- attention rebuilt from each key block's own partial
+  result (out_i, lse_i), combined two at a time with logaddexp weights in a given order;
+  a second implementation used only to pin the first. Pinned by: the same brute force,
+  the page's worked example, and equality with the full row in every order.
 * ``attention.chunk_positions``, ``attention.ring_blocks``, ``attention.allowed_count``,
   ``attention.chunk_units`` -- ownership and counting. Pinned by: the load-balance
   figures the pages print (i+1 units per rank contiguous, 2c+1 zigzag) and exact
@@ -39,4 +40,4 @@ from .attention import (  # noqa: F401
     rank_forward,
     ring_blocks,
 )
-from .fold import online_softmax_fold  # noqa: F401
+from .fold import blockwise_attention, block_partial, combine_partials  # noqa: F401

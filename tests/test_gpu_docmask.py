@@ -50,6 +50,16 @@ def _layout(kind, S, seed):
         pick = rng.random(S) < 0.05
         ds[pick] = np.arange(S)[pick] + 1 + rng.integers(0, 5, pick.sum())
         return ds.astype(np.int32)
+    if kind == "extreme":
+        # starts at or before the sequence start (negative, down to INT32_MIN) see every key
+        # up to the query; starts past the sequence end (up to INT32_MAX) see none
+        ds = doc_start_from_lengths(draw_document_lengths(S, 40, 1.0, seed)).astype(np.int64)
+        u = rng.random(S)
+        ds[u < 0.10] = np.iinfo(np.int32).min
+        ds[(u >= 0.10) & (u < 0.20)] = -rng.integers(1, 1000, ((u >= 0.10) & (u < 0.20)).sum())
+        ds[(u >= 0.20) & (u < 0.25)] = np.iinfo(np.int32).max
+        ds[(u >= 0.25) & (u < 0.30)] = S + rng.integers(0, 1000, ((u >= 0.25) & (u < 0.30)).sum())
+        return ds.astype(np.int32)
     raise ValueError(kind)
 
 
@@ -69,6 +79,9 @@ CASES = [
     (2, 3, 1, 24, 72, 3, 0, False, "f32", "packed"),
     (1, 2, 2, 96, 128, 4, 3, True, "f32", "nonmono"),
     (1, 4, 1, 128, 160, 2, 0, True, "f32", "beyond"),
+    (1, 8, 2, 128, 256, 4, 1, True, "bf16", "extreme"),
+    (1, 4, 1, 128, 192, 3, 2, False, "bf16", "extreme"),
+    (1, 2, 1, 64, 128, 4, 2, True, "f32", "extreme"),
 ]
 
 

@@ -1,6 +1,10 @@
 """Parity at the full sizes of the measured workloads, in the launch configuration the
 bench times (one fused launch over the whole share).
 
+* Every row: the fused launch's out and lse against the oracle on every row of the
+  32k GQA share and of the 64k non-causal workload, and on every row of two query heads
+  per KV group of the 128k GQA share (16 of its 64 heads), at the parity bar over all
+  compared elements. The unchanged oracle runs in host threads, one (batch, head) each.
 * Sampled rows: the oracle computes chosen rows one by one (chunk edges, tile edges,
   random rows, the first and last head of each KV group, every batch) and they are
   compared element by element at the parity bar.
@@ -47,6 +51,83 @@ def workload(request):
     w = WORKLOADS[request.param]
     say(f"generating {w.name}")
     return w, make_inputs(w)
+
+
+PARTS = 4
+
+
+def _every_row_pairs(w):
+    """(batch, query head) pairs compared on every row: all of them, except on the 128k
+    share, where two heads of each KV group are taken (a different position in the group
+    for each group, so every head offset within a group is covered)."""
+    G = w.hq // w.hkv
+    if w.name == "gqa64x8_d128_s128k_c16_zigzag_bf16":
+        heads = sorted({g * G + (g % G) for g in range(w.hkv)} | {g * G + (G - 1 - g % G) for g in range(w.hkv)})
+        return [(b, h) for b in range(w.batch) for h in heads]
+    return [(b, h) for b in range(w.batch) for h in range(w.hq)]
+
+
+@pytest.fixture(scope="module")
+def fused_full(workload):
+    """The bench's launch over the whole share, run once per workload: out (fp32 copy of
+    the bf16 result) and lse on the host, plus the inputs in fp64 for the oracle."""
+    w, (q, k, v) = workload
+    say(f"{w.name}: GPU fused launch (every-row comparison)")
+    out, lse = run_gpu(q, k, v, w.c, w.rank, w.causal, w.zigzag)
+    return out.astype(np.float32), lse, (q.astype(np.float64), k.astype(np.float64), v.astype(np.float64))
+
+
+_EVERY_ROW_STATS = {}
+
+
+def _oracle_heads(w, q64, k64, v64, pairs):
+    """oracle.rank_forward on every row of each (b, h) in pairs, one host thread per pair
+    with single-threaded BLAS (numpy releases the GIL in its array loops)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    n = w.rows
+
+    def one(bh):
+        b, h = bh
+        rows = np.stack([np.full(n, b), np.full(n, h), np.arange(n)], axis=1)
+        return oracle.rank_forward(q64, k64, v64, w.c, w.rank, w.causal, w.zigzag, rows=rows)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(pairs)))
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(one, pairs))
+
+
+@pytest.mark.parametrize("part", range(PARTS))
+def test_every_row_against_oracle(workload, fused_full, part):
+    w, _ = workload
+    out, lse, (q64, k64, v64) = fused_full
+    pairs = _every_row_pairs(w)[part::PARTS]
+    say(f"{w.name}: oracle on every row of {len(pairs)} (batch, head) pairs: {pairs}")
+    res = _oracle_heads(w, q64, k64, v64, pairs)
+    got = np.stack([out[b, h] for b, h in pairs]).astype(np.float64)
+    got_lse = np.stack([lse[b, h] for b, h in pairs])
+    ref = np.stack([r[0] for r in res])
+    ref_lse = np.stack([r[1] for r in res])
+    mx, mean = assert_parity(got, ref, got_lse, ref_lse, "bf16", f"{w.name} part {part}")
+    m = w.rows // 2
+    early, late = (slice(0, m), slice(m, None)) if w.causal else (slice(0, w.rows), slice(0, 0))
+    rel_e = rel_l2(got[:, early], ref[:, early])
+    rel_l = rel_l2(got[:, late], ref[:, late]) if w.causal else float("nan")
+    lse_err = float(np.abs(got_lse - ref_lse).max())
+    say(f"{w.name} part {part}: {got.shape[0] * got.shape[1]} rows, max abs {mx:.2e} mean abs {mean:.2e} "
+        f"lse max abs {lse_err:.2e} rel-L2 early {rel_e:.2e} late {rel_l:.2e}")
+    st = _EVERY_ROW_STATS.setdefault(w.name, {"max": 0.0, "sum": 0.0, "count": 0, "lse": 0.0, "rows": 0})
+    st["max"] = max(st["max"], mx)
+    st["sum"] += float(np.abs(got - ref).sum())
+    st["count"] += got.size
+    st["lse"] = max(st["lse"], lse_err)
+    st["rows"] += got.shape[0] * got.shape[1]
+    say(f"{w.name} so far: {st['rows']} rows, max abs {st['max']:.2e} mean abs {st['sum'] / st['count']:.2e} "
+        f"lse max abs {st['lse']:.2e}")
+    assert st["sum"] / st["count"] <= 2e-3
+    assert rel_l2(got, ref) < 1e-2
 
 
 def test_sampled_rows_against_oracle(workload):

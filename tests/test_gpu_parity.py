@@ -186,6 +186,32 @@ def test_binding_rejects_bad_tensors():
     k2 = torch.zeros((2, 1, 2, 64, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         ra.rank_forward(torch.zeros((1, 4, 64, 96), dtype=torch.bfloat16, device="cuda"), k2, k2, 2, 0, True, True)
+    # preallocated results: host lse, wrong shapes, dtypes or layouts are refused before any launch
+    kk = torch.zeros((2, 1, 2, 64, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        ra.rank_forward(q, kk, kk, 2, 0, True, True, lse=torch.empty((1, 4, 64), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        ra.rank_forward_accumulate(q, kk, kk, torch.empty_like(q), torch.empty((1, 4, 64), dtype=torch.float32),
+                                   2, 0, True, True)
+    with pytest.raises(ValueError):
+        ra.rank_forward(q, kk, kk, 2, 0, True, True, out=torch.empty_like(q, device="cpu"))
+    oa = torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda")
+    la = torch.zeros((4,), dtype=torch.float32, device="cuda")
+    bad_outs = [torch.empty((3, 128), dtype=torch.bfloat16, device="cuda"),     # too small
+                torch.empty((4, 128), dtype=torch.float32, device="cuda"),      # other dtype
+                torch.empty((4, 128), dtype=torch.bfloat16),                    # host memory
+                torch.empty((128, 4), dtype=torch.bfloat16, device="cuda").t()]  # not contiguous
+    for bo in bad_outs:
+        with pytest.raises(ValueError):
+            ra.merge(oa, la, oa, la, out=bo)
+    bad_lses = [torch.empty((3,), dtype=torch.float32, device="cuda"),
+                torch.empty((4,), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((4,), dtype=torch.float32)]
+    for bl in bad_lses:
+        with pytest.raises(ValueError):
+            ra.merge(oa, la, oa, la, lse=bl)
+    with pytest.raises(ValueError):
+        ra.merge(oa, la.cpu(), oa, la)
 
 
 def test_causal_mask_regression_inputs():

@@ -1,7 +1,8 @@
 """Pins of the fp64 oracle to things other than itself (CPU only).
 
 * 50-digit brute force on tiny inputs, every mode (mask, zigzag, GQA).
-* The independent online-softmax fold in every block order, and on unequal re-splits.
+* Attention rebuilt from per-block partial results (each block's own softmax, combined
+  with logaddexp weights) in every block order, and on unequal re-splits.
 * The pages' worked example (q 4x8, k/v 12x8, 3 blocks; allclose at atol 1e-6).
 * torch's fp64 scaled_dot_product_attention (is_causal, enable_gqa) on the full sequence.
 * Zigzag/contiguous shares gathered out of full-sequence causal attention.
@@ -88,7 +89,7 @@ def test_page_worked_example():
     kb = np.stack(np.split(kf, nb))[:, None, None]
     vb = np.stack(np.split(vf, nb))[:, None, None]
     full, _ = oracle.rank_forward(q[None, None], kb, vb, nb, 0, False, False)
-    ring, _ = oracle.online_softmax_fold(q, np.split(kf, nb), np.split(vf, nb))
+    ring, _ = oracle.blockwise_attention(q, np.split(kf, nb), np.split(vf, nb))
     assert np.allclose(full[0, 0], ring, atol=g["atol"]) == g["expected_allclose"]
     np.testing.assert_allclose(full[0, 0], ring, rtol=0, atol=1e-13)
 
@@ -107,7 +108,7 @@ def _share_blocks_with_masks(qg, kg, vg, c, rank, zigzag, causal, b, h):
 
 
 @pytest.mark.parametrize("causal,zigzag", [(False, False), (True, False), (True, True)])
-def test_t2_fold_any_order_equals_full_row(causal, zigzag):
+def test_t2_blockwise_any_order_equals_full_row(causal, zigzag):
     c, S, d, hq, hkv = 4, 32, 8, 2, 1
     qg, kg, vg = _global(1, hq, hkv, S, d, seed=5)
     for rank in range(c):
@@ -116,13 +117,13 @@ def test_t2_fold_any_order_equals_full_row(causal, zigzag):
         for h in range(hq):
             qr, ks, vs, ms = _share_blocks_with_masks(qg, kg, vg, c, rank, zigzag, causal, 0, h)
             for order in itertools.permutations(range(c)):
-                o, l = oracle.online_softmax_fold(qr, [ks[i] for i in order], [vs[i] for i in order],
+                o, l = oracle.blockwise_attention(qr, [ks[i] for i in order], [vs[i] for i in order],
                                                   [ms[i] for i in order])
                 np.testing.assert_allclose(o, full_out[0, h], rtol=0, atol=1e-12)
                 np.testing.assert_allclose(l, full_lse[0, h], rtol=0, atol=1e-12)
 
 
-def test_t2_fold_unequal_resplits():
+def test_t2_blockwise_unequal_resplits():
     c, S, d = 6, 48, 8
     qg, kg, vg = _global(1, 1, 1, S, d, seed=7)
     r = _rng(70)
@@ -136,7 +137,7 @@ def test_t2_fold_unequal_resplits():
             perm = r.permutation(S)
             cuts = np.sort(r.choice(np.arange(1, S), size=r.integers(1, 8), replace=False))
             parts = np.split(perm, cuts)
-            o, l = oracle.online_softmax_fold(q[0, 0], [allk[p] for p in parts], [allv[p] for p in parts],
+            o, l = oracle.blockwise_attention(q[0, 0], [allk[p] for p in parts], [allv[p] for p in parts],
                                               [mask[:, p] for p in parts])
             np.testing.assert_allclose(o, full_out[0, 0], rtol=0, atol=1e-12)
             np.testing.assert_allclose(l, full_lse[0, 0], rtol=0, atol=1e-12)
@@ -377,3 +378,23 @@ def test_t8_document_allowed_counts():
     for zigzag in (False, True):
         total = sum(oracle.allowed_count(c, r, rows, True, zigzag, doc_start=ds) for r in range(c))
         assert total == int(np.sum(np.arange(S) - ds + 1))
+
+
+def test_t7_merge_equals_logspace_combination():
+    """oracle.merge against the log-space combination of two partials (written apart from
+    it in oracle/fold.py), on random partials with empty rows on either or both sides."""
+    r = _rng(77)
+    R, dv = 64, 8
+    oa, ob = r.standard_normal((R, dv)), r.standard_normal((R, dv))
+    la, lb = r.standard_normal(R) * 5, r.standard_normal(R) * 5
+    la[:8] = -np.inf
+    lb[4:12] = -np.inf
+    oa[:8] = 0.0
+    ob[4:12] = 0.0
+    got_o, got_l = oracle.merge(oa, la, ob, lb)
+    ref_o, ref_l = oracle.combine_partials([(oa, la), (ob, lb)])
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    np.testing.assert_allclose(got_l[fin], ref_l[fin], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(got_o, ref_o, rtol=0, atol=1e-13)
+    assert np.all(got_o[4:8] == 0.0) and np.all(np.isneginf(got_l[4:8]))   # empty on both sides
