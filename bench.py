@@ -33,6 +33,7 @@ METRIC = "attention TFLOP/s (unmasked) per rank share, 1 GPU; % of bf16 MFMA pea
 DEFAULT_WORKLOAD = "gqa64x8_d128_s128k_c16_zigzag_bf16"
 ALSO_WORKLOADS = ["gqa32x8_d128_s32k_c8_zigzag_bf16", "mha16_b2_d128_s64k_c8_noncausal_outliers_bf16"]
 MIN_TIMED_MS = 200.0   # short workloads get more steps so the timed region spans this much
+WARMUP_MS = 1000.0     # warmup runs at least this long: the chip's clock ramps up under load
 KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_ring_attention_amd", "csrc", f)
                   for f in ("ra_fwd.hip", "ra_internal.h")]
 
@@ -124,13 +125,14 @@ class ClockSampler:
     def result(self):
         if not self.samples:
             return {"error": self.error or "no samples"}
-        r = {"gfx_mhz_mean": round(float(np.mean(self.samples)), 1), "gfx_mhz_min": float(np.min(self.samples)),
-             "gfx_mhz_max": float(np.max(self.samples)), "samples": len(self.samples),
+        r = {"gfx_mhz_median": float(np.median(self.samples)), "gfx_mhz_mean": round(float(np.mean(self.samples)), 1),
+             "gfx_mhz_min": float(np.min(self.samples)), "gfx_mhz_max": float(np.max(self.samples)),
+             "samples": len(self.samples),
              "source": f"amdsmi gpu_metrics current_gfxclk, polled every {self.period_s * 1e3:.0f} ms "
                        "during the timed launches"}
         if self.xcd:
             width = min(len(x) for x in self.xcd)
-            r["per_xcd_mhz_mean"] = [round(float(np.mean([x[i] for x in self.xcd])), 1) for i in range(width)]
+            r["per_xcd_mhz_median"] = [float(np.median([x[i] for x in self.xcd])) for i in range(width)]
         if self.power:
             r["socket_power_w_mean"] = round(float(np.mean(self.power)), 1)
         if self.error:
@@ -188,7 +190,11 @@ def workload_numbers(w):
     return flop, nbytes
 
 
-def time_workload(w, steps: int, warmup: int, arrays=None, clock=None):
+def time_workload(w, steps: int, warmup: int, arrays=None, clock=None, warmup_ms: float = WARMUP_MS):
+    """Time `steps` launches after at least `warmup` untimed ones, and after as many more
+    as it takes for the warmup to last `warmup_ms` (the graphics clock settles under load
+    over tens of launches). Returns (ms per step by wall clock, mean / min / median kernel
+    ms by HIP events, warmup steps run)."""
     import torch
     import blockwise_ring_attention_amd as ra
     qd, kd, vd = _device_inputs(w, arrays)
@@ -199,8 +205,13 @@ def time_workload(w, steps: int, warmup: int, arrays=None, clock=None):
     def step():
         fwd(qd, kd, vd, out=out, lse=lse, with_lse=w.with_lse)
 
-    for _ in range(warmup):
+    done = 0
+    t_w = time.perf_counter()
+    while done < warmup or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
         step()
+        done += 1
+        if done >= warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     # Kernel time: HIP events on the stream the kernel is launched on (torch's current one).
     stream = torch.cuda.current_stream()
@@ -220,18 +231,20 @@ def time_workload(w, steps: int, warmup: int, arrays=None, clock=None):
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     del qd, kd, vd, out, lse
     torch.cuda.empty_cache()
-    return wall / steps * 1e3, sum(launch_ms) / len(launch_ms), min(launch_ms), float(np.median(launch_ms))
+    return (wall / steps * 1e3, sum(launch_ms) / len(launch_ms), min(launch_ms), float(np.median(launch_ms)),
+            done)
 
 
-def time_workload_min(w, steps: int, warmup: int, arrays=None, min_ms: float = MIN_TIMED_MS):
+def time_workload_min(w, steps: int, warmup: int, arrays=None, min_ms: float = MIN_TIMED_MS, clock=None,
+                      warmup_ms: float = WARMUP_MS):
     """time_workload, run again with more steps when `steps` launches last less than
-    `min_ms` (short launches are timed before the clocks settle). Returns its four
-    figures and the step count of the run reported."""
-    r = time_workload(w, steps, warmup, arrays)
-    if steps * r[0] < min_ms:
-        steps = int(np.ceil(min_ms / r[0]))
-        r = time_workload(w, steps, warmup, arrays)
-    return (*r, steps)
+    `min_ms`. Returns its four timing figures, the step count of the run reported and its
+    warmup steps."""
+    r = time_workload(w, steps, warmup, arrays, warmup_ms=warmup_ms)
+    if steps * r[0] < min_ms or clock is not None:
+        steps = max(steps, int(np.ceil(min_ms / r[0])))
+        r = time_workload(w, steps, warmup, arrays, clock=clock, warmup_ms=warmup_ms)
+    return (*r[:4], steps, r[4])
 
 
 def _device_inputs(w, arrays):
@@ -353,7 +366,7 @@ def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumul
     return ms_step, round_ms, merge_ms, diff, lse_diff
 
 
-def balance_sweep(w, steps: int, warmup: int):
+def balance_sweep(w, steps: int, warmup: int, warmup_ms: float = WARMUP_MS):
     """Every rank r = 0..c-1 of the workload, once with contiguous chunks and once with
     the zigzag pairing (causal), each a fused launch: ms per rank and the spread. Q is the
     same array for every rank (its values do not change the work). Each rank is timed
@@ -369,7 +382,7 @@ def balance_sweep(w, steps: int, warmup: int):
         ranks = []
         for r in range(w.c):
             wr = dataclasses.replace(w, rank=r, zigzag=zig)
-            ms, ml, mn, _, steps_r = time_workload_min(wr, steps, warmup, arrays)
+            ms, ml, mn, _, steps_r, _ = time_workload_min(wr, steps, warmup, arrays, warmup_ms=warmup_ms)
             if ds is None:
                 e = acc.allowed_entries(w.c, r, w.rows, w.rows, True, zig)
             else:
@@ -493,7 +506,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=3, help="untimed launches before the timed ones (at least)")
+    ap.add_argument("--warmup-ms", type=float, default=WARMUP_MS,
+                    help="the warmup also lasts at least this long: the graphics clock settles under load")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle's CPU rate")
     ap.add_argument("--no-also", action="store_true", help="skip the other workloads timed beside the main one")
@@ -504,6 +519,9 @@ def main():
                     help="only run the all-rank sweep (contiguous vs zigzag chunks) of the workload and print it")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum length of the timed oracle run for cpu_baseline")
+    ap.add_argument("--lib", default=None, metavar="NAME_OR_PATH",
+                    help="time another build of the library with the same C ABI: a design-choice ablation "
+                         "name (xcd_scatter, no_swizzle, no_skip, one_head, built by the build script) or a path")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (to scale the "
                          "FETCH_SIZE/WRITE_SIZE counters against a kernel of known traffic)")
@@ -529,17 +547,23 @@ def main():
     if not os.path.exists(_binding.LIB_PATH):
         from blockwise_ring_attention_amd.csrc import build
         build.build()
+    lib_used = None
+    if args.lib:
+        from blockwise_ring_attention_amd.csrc import build
+        lib_used = args.lib if os.path.sep in args.lib else build.ablation_path(args.lib)
+        _binding.use_library(lib_used)
     from blockwise_ring_attention_amd.inputs import make_inputs
     w = WORKLOADS[args.workload]
     if args.balance:
-        sweep = balance_sweep(w, args.steps, args.warmup)
+        sweep = balance_sweep(w, args.steps, args.warmup, args.warmup_ms)
         print(json.dumps({"balance_sweep": w.name, "c": w.c, "seq": w.seq, "steps": args.steps,
                           "warmup": args.warmup, **sweep}), flush=True)
         return
     flop, nbytes = workload_numbers(w)
     arrays = make_inputs(w)
     clock = ClockSampler()
-    ms_step, ms_launch, ms_min, ms_med = time_workload(w, args.steps, args.warmup, arrays, clock=clock)
+    ms_step, ms_launch, ms_min, ms_med, warm_done = time_workload(w, args.steps, args.warmup, arrays, clock=clock,
+                                                                 warmup_ms=args.warmup_ms)
     value = flop / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flop / (ms_launch * 1e-3) / 1e12
@@ -550,7 +574,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warm_done,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -567,10 +591,13 @@ def main():
                      "algorithmic_bytes": nbytes, "kernel_ms_avg": round(ms_launch, 4),
                      "kernel_ms_min": round(ms_min, 4), "kernel_ms_median": round(ms_med, 4)},
     }
+    if lib_used:
+        line["library"] = os.path.relpath(lib_used, ROOT)
+        line["roofline"]["traffic"] = None   # the committed counters describe the shipped kernel
     clk = clock.result()
-    if "gfx_mhz_mean" in clk:
+    if "gfx_mhz_median" in clk:
         # the nominal peak assumes 2.4 GHz; at the clock held under this load it is lower
-        clk["peak_at_observed_clock_tflops"] = round(peak * clk["gfx_mhz_mean"] / 2400.0, 1)
+        clk["peak_at_observed_clock_tflops"] = round(peak * clk["gfx_mhz_median"] / 2400.0, 1)
         clk["frac_of_peak_at_observed_clock"] = round(achieved / clk["peak_at_observed_clock_tflops"], 4)
     line["clock"] = clk
     line["context"] = break_even_context(w, ms_launch, achieved)
@@ -580,11 +607,15 @@ def main():
             wa = WORKLOADS[name]
             fa, _ = workload_numbers(wa)
             arrays_a = make_inputs(wa)
-            ms_a, ml_a, _, _, steps_a = time_workload_min(wa, args.steps, args.warmup, arrays_a)
+            clock_a = ClockSampler()
+            ms_a, ml_a, _, _, steps_a, warm_a = time_workload_min(wa, args.steps, args.warmup, arrays_a,
+                                                                   clock=clock_a, warmup_ms=args.warmup_ms)
             del arrays_a
+            ca = clock_a.result()
             also.append({"workload": name, "value": round(fa / (ms_a * 1e-3) / 1e12, 2), "ms_per_step": round(ms_a, 4),
-                         "kernel_ms_avg": round(ml_a, 4), "steps": steps_a,
-                         "pct_of_peak": round(100 * fa / (ms_a * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)})
+                         "kernel_ms_avg": round(ml_a, 4), "steps": steps_a, "warmup": warm_a,
+                         "pct_of_peak": round(100 * fa / (ms_a * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                         "gfx_mhz_median": ca.get("gfx_mhz_median")})
         line["also"] = also
     if not args.no_per_round:
         what = {"accumulate": "one ra_rank_forward_accumulate launch per ring round (rounds [t, t+1)), each "

@@ -60,6 +60,14 @@ def load(path: str | None = None) -> ctypes.CDLL:
     return lib
 
 
+def use_library(path: str) -> ctypes.CDLL:
+    """Make the library at `path` (same C ABI: a design-choice comparison build made by
+    the build script) the one every later call goes through."""
+    global _lib
+    _lib = load(path)
+    return _lib
+
+
 def last_error() -> str:
     return load().ra_last_error().decode()
 

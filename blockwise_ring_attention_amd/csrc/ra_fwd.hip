@@ -18,6 +18,16 @@
 
 #include <stdint.h>
 
+// Design-choice ablations. The shipped library defines none of these; the build script
+// compiles one extra library per switch, each computing the same result another way, so
+// that the counters and times of a choice can be compared with the kernel that makes it:
+//   RA_ABLATION_XCD_SCATTER  the k-th tile of XCD x reads KV head (x + k) mod 8, so every
+//                            XCD streams every KV head (no L2 locality per KV head);
+//   RA_ABLATION_NO_SWIZZLE   K and V rows unswizzled in LDS (bank conflicts on the reads);
+//   RA_ABLATION_NO_SKIP      every KV row of every round visited, every entry masked by
+//                            predicate instead of skipped (no causal tile skipping);
+//   RA_ABLATION_ONE_HEAD     one query head per workgroup (no GQA head packing; ra_host.cpp).
+
 namespace ra {
 namespace {
 
@@ -66,7 +76,11 @@ __device__ inline Tile decode_tile(const FwdArgs& a) {
     qrank = k / per;
     const int rem = k % per;
     hset = rem % a.hsets;
+#if defined(RA_ABLATION_XCD_SCATTER)
+    bg = ((xcd + k) & 7) + 8 * (rem / a.hsets);
+#else
     bg = xcd + 8 * (rem / a.hsets);
+#endif
   } else {
     const int stream = w % a.streams;
     qrank = w / a.streams;
@@ -136,11 +150,16 @@ struct KvCursor {
     mrow = slim - 32;
     mlow = -1;
     if (a.causal) {
+#if defined(RA_ABLATION_NO_SKIP)
+      mrow = -1;            // every run of every row takes the per-entry mask
+      mlow = 0x7fffffff;
+#else
       const int lim = q.hi - pdelta + 1;   // rows whose position <= the last query's
       rend = max(r0, min(rend, lim));
       mrow = min(mrow, q.lo - pdelta - 31);
       mlow = q.dmax - pdelta;
       r0 = max(r0, q.dmin - pdelta);
+#endif
     }
     r = r0;
     return r < rend;
@@ -282,8 +301,13 @@ struct Bf16Layout {
   // V tiles follow the NB K tiles in LDS; V^T fragment offsets carry this bias (see the
   // kernel) so that a V tile address minus the bias fits the 16-bit read offset.
   static constexpr int kVBias = NB * TILE >= 65536 ? 65536 : 0;
+#if defined(RA_ABLATION_NO_SWIZZLE)
+  static __device__ inline int kswz(int) { return 0; }
+  static __device__ inline int vswz(int) { return 0; }
+#else
   static __device__ inline int kswz(int row) { return (row / RPL) & (CPR - 1); }
   static __device__ inline int vswz(int row) { return 4 * ((row / RPL) & (CPR / 4 - 1)); }
+#endif
 };
 
 // Issue one stage's K and V tiles (rows r .. r+BN-1 of one (block, batch, KV head) slab)

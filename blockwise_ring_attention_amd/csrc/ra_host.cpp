@@ -95,7 +95,11 @@ int forward(const void* q, const void* k_blocks, const void* v_blocks, const int
   a.c = c; a.rank = rank; a.causal = is_causal; a.zigzag = is_zigzag; a.t0 = round_begin; a.t1 = round_end;
   const int col_blocks = dtype == RA_BF16 ? ra::kBf16ColBlocks : ra::kF32ColBlocks;
   a.G = hq / hkv;
+#if defined(RA_ABLATION_ONE_HEAD)
+  a.hpw = dtype == RA_BF16 ? 1 : heads_per_workgroup(a.G, col_blocks);   // design-choice ablation, see ra_fwd.hip
+#else
   a.hpw = heads_per_workgroup(a.G, col_blocks);
+#endif
   a.hsets = a.G / a.hpw;
   a.prow = 32 * (col_blocks / a.hpw);
   a.nhalves = is_zigzag ? 2 : 1;

@@ -225,3 +225,17 @@ def test_sweep_configurations_are_valid():
         flags.add((p["causal"], p["zigzag"], p["dtype"]))
     assert modes == {"fused", "doc", "accumulate"}
     assert len(flags) >= 7
+
+
+def test_ablation_libraries_export_the_boundary():
+    """The design-choice comparison builds (made by the build script beside libra.so) load
+    and export every entry point the header declares, so the bench can time them through
+    the same calls."""
+    from blockwise_ring_attention_amd.csrc import build
+    for name in build.ABLATIONS:
+        path = build.ablation_path(name)
+        if not os.path.exists(path):
+            pytest.skip(f"{path} not built (build_ablations)")
+        lib = ctypes.CDLL(path)
+        for sym in _declared_functions():
+            assert hasattr(lib, sym), (name, sym)
