@@ -31,7 +31,8 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x
 PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 matrix
 METRIC = "attention TFLOP/s (unmasked) per rank share, 1 GPU; % of bf16 MFMA peak"
 DEFAULT_WORKLOAD = "gqa64x8_d128_s128k_c16_zigzag_bf16"
-ALSO_WORKLOADS = ["gqa32x8_d128_s32k_c8_zigzag_bf16", "mha16_b2_d128_s64k_c8_noncausal_outliers_bf16"]
+ALSO_WORKLOADS = ["gqa32x8_d128_s32k_c8_zigzag_bf16", "mha16_b2_d128_s64k_c8_noncausal_outliers_bf16",
+                  "mha_d64_s4k_c4_zigzag_fp32"]
 MIN_TIMED_MS = 200.0   # short workloads get more steps so the timed region spans this much
 WARMUP_MS = 1000.0     # warmup runs at least this long: the chip's clock ramps up under load
 KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_ring_attention_amd", "csrc", f)
@@ -205,7 +206,10 @@ def time_workload(w, steps: int, warmup: int, arrays=None, clock=None, warmup_ms
     def step():
         fwd(qd, kd, vd, out=out, lse=lse, with_lse=w.with_lse)
 
-    done = 0
+    # the first launch also loads the library's code objects: it does not count as warmup time
+    step()
+    torch.cuda.synchronize()
+    done = 1
     t_w = time.perf_counter()
     while done < warmup or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
         step()
@@ -434,6 +438,50 @@ def break_even_context(w, kernel_ms: float, tflops: float):
     return ctx
 
 
+def sustain_run(w, seconds: float, flop: float, buckets: int = 12):
+    """Launch the workload back to back for `seconds`, starting from an idle GPU, timing
+    every launch with HIP events and sampling the clock and power every 20 ms: the
+    throughput of each consecutive slice of the run, and the samples of that slice."""
+    import torch
+    qd, kd, vd = _device_inputs(w, None)
+    fwd = _forward_fn(w)
+    out = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
+    fwd(qd, kd, vd, out=out, lse=lse)
+    torch.cuda.synchronize()
+    t_one = time.perf_counter()
+    fwd(qd, kd, vd, out=out, lse=lse)
+    torch.cuda.synchronize()
+    n = max(buckets, int(seconds / max(1e-4, time.perf_counter() - t_one)))
+    time.sleep(2.0)   # idle first
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    clock = ClockSampler(period_s=0.02)
+    stamps = []
+    clock.__enter__()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record()
+        fwd(qd, kd, vd, out=out, lse=lse)
+        e1.record()
+    torch.cuda.synchronize()
+    clock.__exit__(None, None, None)
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    per = n // buckets
+    rows = []
+    t = 0.0
+    for i in range(buckets):
+        seg = ms[i * per:(i + 1) * per]
+        rows.append({"launches": [i * per, (i + 1) * per - 1], "start_s": round(t / 1e3, 3),
+                     "kernel_ms": round(float(seg.mean()), 4), "tflops": round(flop / (seg.mean() * 1e-3) / 1e12, 1)})
+        t += float(seg.sum())
+    res = {"launches": n, "seconds": round(time.perf_counter() - t0, 2), "slices": rows,
+           "clock": clock.result(), "clock_samples": [round(x) for x in clock.samples],
+           "power_samples": [round(x) for x in clock.power]}
+    del qd, kd, vd, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_sample(w, count: int):
     """`count` query rows of batch 0 spread evenly over the share (head-major order), so
     light and heavy rows of a causal share enter in proportion, and the unmasked FLOP of
@@ -517,6 +565,9 @@ def main():
                          "(out, lse), with an fp32 or bf16 running out, or plain launches plus ra_merge)")
     ap.add_argument("--balance", action="store_true",
                     help="only run the all-rank sweep (contiguous vs zigzag chunks) of the workload and print it")
+    ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
+                    help="only run the workload back to back for SECONDS from idle and print the throughput "
+                         "and the sampled clock and power over time")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum length of the timed oracle run for cpu_baseline")
     ap.add_argument("--lib", default=None, metavar="NAME_OR_PATH",
@@ -560,6 +611,9 @@ def main():
                           "warmup": args.warmup, **sweep}), flush=True)
         return
     flop, nbytes = workload_numbers(w)
+    if args.sustain:
+        print(json.dumps({"sustain": w.name, **sustain_run(w, args.sustain, flop)}), flush=True)
+        return
     arrays = make_inputs(w)
     clock = ClockSampler()
     ms_step, ms_launch, ms_min, ms_med, warm_done = time_workload(w, args.steps, args.warmup, arrays, clock=clock,
@@ -614,7 +668,9 @@ def main():
             ca = clock_a.result()
             also.append({"workload": name, "value": round(fa / (ms_a * 1e-3) / 1e12, 2), "ms_per_step": round(ms_a, 4),
                          "kernel_ms_avg": round(ml_a, 4), "steps": steps_a, "warmup": warm_a,
-                         "pct_of_peak": round(100 * fa / (ms_a * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                         "pct_of_peak": round(100 * fa / (ms_a * 1e-3) / 1e12 /
+                                              (PEAK_BF16_TFLOPS if wa.dtype == "bf16" else PEAK_F32_TFLOPS), 2),
+                         "peak_tflops": PEAK_BF16_TFLOPS if wa.dtype == "bf16" else PEAK_F32_TFLOPS,
                          "gfx_mhz_median": ca.get("gfx_mhz_median")})
         line["also"] = also
     if not args.no_per_round:
