@@ -547,6 +547,9 @@ def cpu_baseline(w, arrays, min_seconds: float = 10.0):
                    f"a full fp64 row against all {w.c * w.rows} keys (masked entries computed and discarded); "
                    f"{sec:.1f} s wall; rate counts unmasked work only"),
         "seconds": sec,
+        # every oracle row costs the same (a full row against every key), so the whole
+        # share (all batches, heads and rows) scales linearly from the sample
+        "full_share_seconds_estimate": round(sec * w.batch * total_rows / count, 1),
     }
 
 
