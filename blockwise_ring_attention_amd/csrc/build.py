@@ -27,6 +27,7 @@ ABLATIONS = {
     "no_swizzle": "RA_ABLATION_NO_SWIZZLE",
     "no_skip": "RA_ABLATION_NO_SKIP",
     "one_head": "RA_ABLATION_ONE_HEAD",
+    "stage_barrier": "RA_ABLATION_STAGE_BARRIER",
 }
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU forms are kept out of every kernel. Inputs are taken to be NaN-free,

@@ -26,7 +26,9 @@
 //   RA_ABLATION_NO_SWIZZLE   K and V rows unswizzled in LDS (bank conflicts on the reads);
 //   RA_ABLATION_NO_SKIP      every KV row of every round visited, every entry masked by
 //                            predicate instead of skipped (no causal tile skipping);
-//   RA_ABLATION_ONE_HEAD     one query head per workgroup (no GQA head packing; ra_host.cpp).
+//   RA_ABLATION_ONE_HEAD     one query head per workgroup (no GQA head packing; ra_host.cpp);
+//   RA_ABLATION_STAGE_BARRIER a workgroup barrier before every stage instead of every pair
+//                            of stages.
 
 namespace ra {
 namespace {
@@ -275,9 +277,10 @@ __device__ inline RowFold fold_row(bool accumulate, float lse_old, float mref, f
 // SIMD): every K/V stage staged in LDS serves 256 query columns.
 //
 // K/V stages of BN = 64 keys go straight from global memory into LDS (buffer loads that
-// write LDS), so no VGPRs are spent on staging; of the NB stage buffers, the one being
-// folded and the previous one (whose V tile the first step still reads) are in use, and
-// the loads of the next NB - 2 stages fill the others. Rows are 2*D bytes, unpadded; 16-byte chunks are
+// write LDS), so no VGPRs are spent on staging. NB = 4 buffers each for K and V tiles;
+// stages are folded in pairs with one workgroup barrier per pair, and each pair loads the
+// K tiles of the next pair and the V tiles one stage behind them (see the kernel). Rows
+// are 2*D bytes, unpadded; 16-byte chunks are
 // XOR-swizzled per row so that both the K fragment reads (ds_read_b128, 16 rows per pass)
 // and the V^T transpose reads (ds_read_b64_tr_b16, 4 rows x 4 chunks per pass) hit
 // distinct banks.
@@ -383,7 +386,8 @@ struct StageLoader {
 };
 
 // Wait until at most STAGES stages of this thread's K/V loads are still in flight (loads
-// complete in issue order; every stage issues the same number of them).
+// complete in issue order; every stage issues the same number of them). STAGES = 0 waits
+// for every load of the thread.
 template <int D, int STAGES>
 __device__ __forceinline__ void wait_stages() {
   constexpr int N = STAGES * 2 * Bf16Layout<D>::LOADS;   // loads allowed in flight
@@ -393,11 +397,8 @@ __device__ __forceinline__ void wait_stages() {
 
 // Workgroup barrier between phases. No instruction is scheduled across it, and the
 // memory clobber keeps the compiler from moving loads or stores over it. It waits for no
-// memory counter. The LDS reads still in flight when a wave arrives are the first V^T
-// fragments of the next step, from the stage just folded, whose buffer no load issued
-// after this barrier writes (the next load into it comes two barriers later). K/V loads
-// are waited for explicitly (wait_stages), which a workgroup fence would instead drain
-// completely.
+// memory counter: no LDS read is in flight when a wave arrives (the step before a barrier
+// reads nothing ahead), and K/V loads are waited for explicitly (wait_stages) before it.
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
@@ -451,9 +452,10 @@ __device__ inline void mask_sub(const FwdArgs& a, const SubInfo& si, int hf, int
 // across steps: the last products of a step read the first fragments of the next one
 // (NXK: its K fragments from kn, NXV: its V^T fragments from vn), and a step whose first
 // fragments were read that way (PRK, PRV) starts on them at once. The scheduling groups
-// pin the interleave. A stage's first step has only its V^T fragments read ahead (its K
-// tile is complete only after the stage barrier); it issues each P.V product before its
-// QK k-step, so the matrix cores start while the first K fragments are in flight.
+// pin the interleave. The step after a barrier reads its own fragments (the tiles are
+// complete only after the barrier). A step with only its V^T fragments read ahead issues
+// each P.V product before its QK k-step, so the matrix cores start while the first K
+// fragments are in flight.
 constexpr int kAhead = 2;
 
 template <int D>
@@ -709,16 +711,6 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     return ld.plan(kg + off, vg + off, c.r, a.nkv, c.valid != 0);
   };
 
-  // Stage s lives in buffer s % NB and is read by the sub-tile steps 2s-1 and 2s (its K)
-  // and 2s+1 and 2s+2 (its V). Each stage begins with a workgroup barrier, before which
-  // every wave waits for its own loads of stage s: after it, stage s is complete in LDS
-  // for everyone, and stage s - 2 (last read at step 2s - 2) is free, so the loads of
-  // stage s + NB - 2 go into its buffer during stage s. The buffers are distinct arrays
-  // and the loop is unrolled over them, so the compiler can tell a stage's reads apart
-  // from the loads in flight into the other buffers. Even sub-tiles use (sA, pA), odd
-  // ones (sB, pB). Every stage issues its loads, empty ones past the end of the stream,
-  // so the wait before each barrier is the same: all but the last stage issued.
-
   // Accumulate mode: the running (out, lse) of the lane's row, read at the start of the
   // tail (Q fragments are dead by then, so the registers are free) and used by the
   // epilogue, so the read overlaps the last P.V products instead of following them.
@@ -753,32 +745,55 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   const bool cc_any = cc.valid;   // some stage is folded
   if (cc.valid) {
-#pragma unroll
-    for (int st = 0; st < NB - 2; ++st) {
-      const typename StageLoader<D>::Plan pl = plan_next();
-      ld.issue_k(pl, kb[st]);
-      ld.issue_v(pl, vb[st]);
+    // Stages run in pairs (2w, 2w+1) with one workgroup barrier, before the even stage.
+    // Stage k's K tile is read by the steps of stage k (2k-1, 2k), its V tile by those of
+    // stage k+1 (the P.V products lag the scores by two sub-tiles), so the pair (2w,
+    // 2w+1) reads K of 2w, 2w+1 and V of 2w-1, 2w. Those are complete at its barrier:
+    // every wave waits there for all its loads, issued during the previous pair. After
+    // the barrier the pair issues, inside its even stage's steps, the loads of the tiles
+    // the next pair reads: K of 2w+2, 2w+3 and V of 2w+1, 2w+2 (stage k's tiles in buffer
+    // k % NB), into buffers the previous pair has finished with. The V tile of 2w+3 is
+    // planned with its K tile but issued by the next pair (`pend`): its buffer holds V of
+    // 2w-1, which this pair reads. The buffers are distinct arrays and the loop is
+    // unrolled over them, so the compiler can tell a stage's reads apart from the loads
+    // in flight into the other buffers. Even sub-tiles use (sA, pA), odd ones (sB, pB).
+    // Every pair issues its loads, empty ones past the end of the stream (into buffers
+    // nothing reads again), so the loads need no branch and can sit inside the steps.
+    typename StageLoader<D>::Plan pend;
+    {
+      const typename StageLoader<D>::Plan p0 = plan_next();
+      ld.issue_k(p0, kb[0]);
+      ld.issue_v(p0, vb[0]);
+      pend = plan_next();
+      ld.issue_k(pend, kb[1]);
     }
     f32x16 sA, sB;
     bf16x8 pA[2], pB[2];
     Frags<D> fr;   // LDS fragments in flight, read ahead across steps (see pipe_block)
     // ---- stage 0 (buffer 0): steps -1 and 0
-    wait_stages<D, NB - 3>();
+    wait_stages<D, 0>();
     phase_barrier();
-    {
-      const typename StageLoader<D>::Plan pl = plan_next();
-      ld.issue_k(pl, kb[NB - 2]);
-      ld.issue_v(pl, vb[NB - 2]);
-    }
     SubInfo prev = sub_info(cc, 1);
-    pipe_step<D, true, false, false>(a, prev, hf, qds, qpos, sc, kb[0], vb[0], qf, koff, voff, pB, o, sA, sB, pB,
-                                     mref, lsum, fr);
-    // ... and reads the first V^T fragments of stage 0 for step 1
-    pipe_step<D, true, false, true, false, false, false, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
-                                                               kb[0] + 32 * L::ROWB, vb[0], qf, koff, voff, pB, o,
-                                                               sB, sA, pA, mref, lsum, fr, nullptr, vb[0]);
+    {
+      typename StageLoader<D>::Plan pl;
+      pipe_step<D, true, false, false>(a, prev, hf, qds, qpos, sc, kb[0], vb[0], qf, koff, voff, pB, o, sA, sB, pB,
+                                       mref, lsum, fr, nullptr, nullptr, [&] {
+                                         ld.issue_v(pend, vb[1]);
+                                         pl = plan_at(lc);
+                                         ld.issue_k(pl, kb[2]);
+                                       });
+      if (lc.valid) lc.next(a, qr);
+      // ... reads the first K fragments of stage 1 and V^T fragments of stage 0 for step 1
+      pipe_step<D, true, false, true, false, false, true, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
+                                                                kb[0] + 32 * L::ROWB, vb[0], qf, koff, voff, pB, o,
+                                                                sB, sA, pA, mref, lsum, fr, kb[1], vb[0], [&] {
+                                                                  ld.issue_v(pl, vb[2]);
+                                                                  pend = plan_at(lc);
+                                                                  ld.issue_k(pend, kb[3]);
+                                                                });
+      if (lc.valid) lc.next(a, qr);
+    }
     cc.next(a, qr);
-    int s = 1;
     int last = 0;   // buffer of the last stage, for the tail
     if (cc.valid) {
       for (;;) {
@@ -786,33 +801,43 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
         for (int u = 0; u < NB; ++u) {
           // ---- stage s (buffer b); prev describes sub-tile 1 of stage s - 1 (buffer bp)
           const int b = (1 + u) % NB, bp = u % NB;
-          // The first V^T fragments of step 2s-1 (stage s-1's, complete since the last
-          // barrier) were read at the end of step 2s-2; its K fragments wait for this one.
-          wait_stages<D, NB - 3>();
-          phase_barrier();
-          // The K tile of stage s + NB - 2 is issued inside step 2s-1 and its V tile inside
-          // step 2s, between their MFMAs: spreading a stage's loads over the stage, away from
-          // the barrier, beats issuing them in one burst.
-          const int bn = (1 + u + NB - 2) % NB;
-          typename StageLoader<D>::Plan pl;
-          // step 2s-1: S of (s, sub 0); P.V of (s-1, sub 0); softmax of (s-1, sub 1)
-          pipe_step<D, true, true, true, false, true, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf, koff,
-                                                                voff, pA, o, sA, sB, pB, mref, lsum, fr,
-                                                                kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB,
-                                                                [&] {
-                                                                  pl = plan_at(lc);
-                                                                  ld.issue_k(pl, kb[bn]);
-                                                                });
-          // step 2s: S of (s, sub 1); P.V of (s-1, sub 1); softmax of (s, sub 0)
-          // ... and reads the first V^T fragments of stage s for step 2s+1 (or the tail)
-          pipe_step<D, true, true, true, true, true, false, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
-                                                                  kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB, qf,
-                                                                  koff, voff, pB, o, sB, sA, pA, mref, lsum, fr,
-                                                                  nullptr, vb[b], [&] { ld.issue_v(pl, vb[bn]); });
-          if (lc.valid) lc.next(a, qr);
+          if (u % 2 == 0) {
+            // odd s: no barrier; the first fragments of both steps were read ahead
+#if defined(RA_ABLATION_STAGE_BARRIER)
+            phase_barrier();   // design-choice ablation (see the top of this file)
+#endif
+            pipe_step<D, true, true, true, true, true, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf,
+                                                                 koff, voff, pA, o, sA, sB, pB, mref, lsum, fr,
+                                                                 kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB);
+            pipe_step<D, true, true, true, true, true>(a, sub_info(cc, 0), hf, qds, qpos, sc, kb[b] + 32 * L::ROWB,
+                                                       vb[bp] + 32 * L::ROWB, qf, koff, voff, pB, o, sB, sA, pA,
+                                                       mref, lsum, fr);
+          } else {
+            // even s: the pair's barrier; the loads of stages s+2, s+3 (V of s+1, s+2)
+            wait_stages<D, 0>();
+            phase_barrier();
+            typename StageLoader<D>::Plan pl;
+            pipe_step<D, true, true, true, false, false, true, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[bp], qf,
+                                                                   koff, voff, pA, o, sA, sB, pB, mref, lsum, fr,
+                                                                   kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB, [&] {
+                                                                     ld.issue_v(pend, vb[(b + 1) % NB]);
+                                                                     pl = plan_at(lc);
+                                                                     ld.issue_k(pl, kb[(b + 2) % NB]);
+                                                                   });
+            if (lc.valid) lc.next(a, qr);
+            // ... and reads the first K fragments of stage s+1 and V^T fragments of s
+            pipe_step<D, true, true, true, true, true, true, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
+                                                                 kb[b] + 32 * L::ROWB, vb[bp] + 32 * L::ROWB, qf,
+                                                                 koff, voff, pB, o, sB, sA, pA, mref, lsum, fr,
+                                                                 kb[(b + 1) % NB], vb[b], [&] {
+                                                                   ld.issue_v(pl, vb[(b + 2) % NB]);
+                                                                   pend = plan_at(lc);
+                                                                   ld.issue_k(pend, kb[(b + 3) % NB]);
+                                                                 });
+            if (lc.valid) lc.next(a, qr);
+          }
           prev = sub_info(cc, 1);
           cc.next(a, qr);
-          ++s;
           if (!cc.valid) {
             last = b;
             goto tail;
@@ -822,14 +847,23 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     }
   tail:
     read_old();
-    // ---- after the last stage (buffer `last`): steps 2n-1 and 2n
+    // ---- after the last stage (buffer `last`): steps 2n-1 and 2n. After an even stage
+    // its V tile is complete and its first fragments were read ahead; after an odd one
+    // its V tile was issued during that stage's pair, so the workgroup waits for it.
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (b == last) {
-        // the first V^T fragments of each step were read by the step before
-        pipe_step<D, false, true, true, false, true, false, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[b], qf, koff,
-                                                                  voff, pA, o, sA, sB, pB, mref, lsum, fr, nullptr,
-                                                                  vb[b] + 32 * L::ROWB);
+        if (b % 2 == 0) {
+          pipe_step<D, false, true, true, false, true, false, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[b], qf,
+                                                                    koff, voff, pA, o, sA, sB, pB, mref, lsum, fr,
+                                                                    nullptr, vb[b] + 32 * L::ROWB);
+        } else {
+          wait_stages<D, 0>();
+          phase_barrier();
+          pipe_step<D, false, true, true, false, false, false, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[b], qf,
+                                                                     koff, voff, pA, o, sA, sB, pB, mref, lsum, fr,
+                                                                     nullptr, vb[b] + 32 * L::ROWB);
+        }
         pipe_step<D, false, true, false, false, true>(a, prev, hf, qds, qpos, sc, kb[b], vb[b] + 32 * L::ROWB, qf,
                                                       koff, voff, pB, o, sB, sA, pA, mref, lsum, fr);
       }

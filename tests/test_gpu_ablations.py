@@ -2,11 +2,11 @@
 
 The build script compiles one library per design-choice switch (see the top of
 ra_fwd.hip): KV heads scattered over the XCDs, unswizzled LDS rows, no causal tile
-skipping, one query head per workgroup. They exist to measure what each choice is worth,
-so each must give the shipped library's result: bit-identical (every row's keys are folded
-in the same order with the same arithmetic; skipped tiles would only have added exact
-zeros), and within the parity bar of the fp64 oracle. Called through the C ABI of each
-library.
+skipping, one query head per workgroup, a barrier before every stage. They exist to
+measure what each choice is worth, so each must give the shipped library's result:
+bit-identical (every row's keys are folded in the same order with the same arithmetic;
+skipped tiles would only have added exact zeros), and within the parity bar of the fp64
+oracle. Called through the C ABI of each library.
 """
 
 import ctypes
@@ -21,7 +21,7 @@ from tests.gpu_util import assert_parity, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["xcd_scatter", "no_swizzle", "no_skip", "one_head"]
+NAMES = ["xcd_scatter", "no_swizzle", "no_skip", "one_head", "stage_barrier"]
 
 
 def _run(lib_path, q, k, v, c, rank, causal, zigzag):
