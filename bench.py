@@ -420,7 +420,8 @@ def break_even_context(w, kernel_ms: float, tflops: float):
         "pages_break_even_tokens": round(PAGES_H100_TFLOPS * 1e12 / (PAGES_NVLINK_GBPS * 1e9), 1),
         "pages_arithmetic": f"{PAGES_H100_TFLOPS:.0f} TFLOP/s (H100) / {PAGES_NVLINK_GBPS:.0f} GB/s (NVLink) "
                             "= tokens per block at which a block's compute hides its transfer (single head)",
-        "same_arithmetic_mi355x_one_xgmi_link_tokens": round(tflops * 1e12 / (XGMI_LINK_GBPS * 1e9), 1),
+        "same_arithmetic_mi355x_peak_one_xgmi_link_tokens": round(PEAK_BF16_TFLOPS * 1e12 / (XGMI_LINK_GBPS * 1e9), 1),
+        "same_arithmetic_measured_rate_one_xgmi_link_tokens": round(tflops * 1e12 / (XGMI_LINK_GBPS * 1e9), 1),
         "mean_round_ms": round(round_ms, 4),
         "kv_block_bytes": block_bytes,
         "link_gbps_needed_to_hide_a_round": round(block_bytes / (round_ms * 1e-3) / 1e9, 1),
