@@ -151,3 +151,40 @@ def test_cpu_sample_counts_its_rows(name):
         m = A.causal_allowed(pq, pk) if ds is None else A.document_allowed(pq, pk, ds)
         allowed = int(m.sum())
     assert flop == 4 * w.head_dim * allowed
+
+
+def test_bench_break_even_context():
+    """The bench line's ring arithmetic: the pages' H100 figure ("What do you do about long
+    sequences and sparse models?", section "When is the ring actually free?", the golden
+    fixture), the same c >= F / B with this GPU's peak and one xGMI link, and for the
+    zigzag GQA share a non-local round's share of the launch, 2 m^2 of its (2c-1) m^2 +
+    m(m+1) allowed entries per head."""
+    import bench
+    from blockwise_ring_attention_amd.inputs import WORKLOADS
+    g = json.load(open(os.path.join(GOLDEN, "ring_break_even.json")))
+    w = WORKLOADS["gqa64x8_d128_s128k_c16_zigzag_bf16"]
+    ctx = bench.break_even_context(w, kernel_ms=14.0, tflops=1250.0)
+    assert round(ctx["pages_break_even_tokens"]) == g["nvlink_tokens_per_block"]
+    assert ctx["same_arithmetic_mi355x_peak_one_xgmi_link_tokens"] == pytest.approx(2516.6e12 / 153e9, rel=1e-4)
+    assert ctx["same_arithmetic_measured_rate_one_xgmi_link_tokens"] == pytest.approx(1250e12 / 153e9, rel=1e-4)
+    m = w.rows // 2
+    frac = 2 * m * m / ((2 * w.c - 1) * m * m + m * (m + 1))
+    assert ctx["nonlocal_round_ms_at_measured_rate"] == pytest.approx(14.0 * frac, abs=1e-4)
+    assert ctx["kv_block_bytes"] == 2 * w.batch * w.hkv * w.rows * w.head_dim * 2
+    # m >= F Hkv / (L Hq) for the GQA share
+    assert ctx["min_chunk_tokens_to_hide_on_one_link"] == pytest.approx(1250e12 * w.hkv / (153e9 * w.hq), rel=1e-4)
+
+
+def test_bench_traffic_only_for_the_profiled_kernel(monkeypatch):
+    """roofline.traffic comes from the committed counter profile only while the kernel
+    sources still hash to the sha the profile was taken on; otherwise it is null."""
+    import bench
+    rec = json.load(open(os.path.join(os.path.dirname(bench.__file__), "profiles",
+                                      "traffic_gqa64x8_d128_s128k_c16_zigzag_bf16.json")))
+    got = bench.measured_traffic("gqa64x8_d128_s128k_c16_zigzag_bf16", 14.0)
+    if rec["kernel_sha"] == bench.kernel_sha():
+        assert got == pytest.approx(rec["hbm_bytes_per_launch"])
+    else:
+        assert got is None
+    monkeypatch.setattr(bench, "kernel_sha", lambda: "0" * 16)
+    assert bench.measured_traffic("gqa64x8_d128_s128k_c16_zigzag_bf16", 14.0) is None
