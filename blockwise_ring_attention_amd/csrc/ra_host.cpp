@@ -27,6 +27,13 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// Byte ranges [a, a + na) and [b, b + nb) share a byte (empty or NULL ranges share none).
+bool overlaps(const void* a, unsigned long long na, const void* b, unsigned long long nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const unsigned long long x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
 bool head_dim_supported(int dtype, int d) {
   if (dtype == RA_BF16) return d == 64 || d == 128;
   return d >= 8 && d <= 128 && d % 8 == 0;
@@ -87,6 +94,22 @@ int forward(const void* q, const void* k_blocks, const void* v_blocks, const int
   if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
   if (!aligned(doc, 4)) return fail(RA_ERR_ALIGN, "doc_start must be 4-byte aligned");
   if (acc && lse == nullptr) return fail(RA_ERR_ARG, "accumulating needs the running lse (got NULL)");
+  {
+    // The kernels read q, k, v and doc_start while they write out and lse.
+    const unsigned long long rows = (unsigned long long)batch * hq * nq;
+    const unsigned long long q_bytes = rows * head_dim * elem_bytes;
+    const unsigned long long kv_bytes = (unsigned long long)c * batch * hkv * nkv * head_dim * elem_bytes;
+    const unsigned long long out_bytes = rows * head_dim * (out_dtype == RA_F32 ? 4 : 2);
+    const unsigned long long lse_bytes = lse != nullptr ? rows * 4 : 0;
+    const unsigned long long doc_bytes = doc != nullptr ? (unsigned long long)c * nkv * 4 : 0;
+    const void* in[4] = {q, k_blocks, v_blocks, doc};
+    const unsigned long long in_bytes[4] = {q_bytes, kv_bytes, kv_bytes, doc_bytes};
+    for (int i = 0; i < 4; ++i) {
+      if (overlaps(out, out_bytes, in[i], in_bytes[i]) || overlaps(lse, lse_bytes, in[i], in_bytes[i]))
+        return fail(RA_ERR_ARG, "out and lse must not overlap q, k_blocks, v_blocks or doc_start");
+    }
+    if (overlaps(out, out_bytes, lse, lse_bytes)) return fail(RA_ERR_ARG, "out and lse must not overlap");
+  }
 
   ra::FwdArgs a{};
   a.q = q; a.k = k_blocks; a.v = v_blocks; a.out = out; a.lse = lse; a.doc = doc; a.acc = acc ? 1 : 0;

@@ -86,7 +86,7 @@ enum ra_status {
  *
  * nq = 0 or batch = 0 enqueues nothing and returns RA_OK. nkv = 0 (non-causal) or an
  * empty round range writes out = 0 and lse = -inf. Pointers of empty tensors may be
- * NULL.
+ * NULL. out and lse must not overlap each other or any input (RA_ERR_ARG).
  */
 int ra_rank_forward(const void* q, const void* k_blocks, const void* v_blocks,
                     void* out, float* lse,

@@ -160,6 +160,33 @@ def test_forward_accumulate_argument_errors(ra_lib, kw, code):
     assert B.last_error() != ""
 
 
+# distinct 16-byte aligned fake addresses, 1 MiB apart (larger than any tensor below)
+QA, KA, VA, OA, LA, DA = (0x100000 * i for i in range(1, 7))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(out=QA),                  # out is q
+    dict(out=KA + 4096),           # out starts inside k_blocks
+    dict(lse=VA + 65536),          # lse inside v_blocks
+    dict(out=QA + 32768),          # out starts inside q
+    dict(lse=OA + 1024),           # lse inside out
+    dict(out=LA - 16),             # out ends inside lse
+])
+def test_forward_outputs_must_not_overlap_inputs(ra_lib, kw):
+    a = dict(q=QA, k=KA, v=VA, out=OA, lse=LA)
+    a.update(kw)
+    assert _fwd(**a) == B.RA_ERR_ARG
+    assert "overlap" in B.last_error()
+    assert _fwd_acc(**a) == B.RA_ERR_ARG
+    assert _fwd_acc(**a, out_dtype=B.RA_F32) == B.RA_ERR_ARG
+
+
+def test_forward_doc_outputs_must_not_overlap_doc_start(ra_lib):
+    assert _fwd_doc(q=QA, k=KA, v=VA, doc=DA, out=DA + 512, lse=LA) == B.RA_ERR_ARG
+    assert _fwd_doc(q=QA, k=KA, v=VA, doc=DA, out=OA, lse=DA - 16) == B.RA_ERR_ARG
+    assert "overlap" in B.last_error()
+
+
 def test_forward_accumulate_empty_is_a_noop(ra_lib):
     assert _fwd_acc(batch=0, q=0, k=0, v=0, out=0, lse=0) == B.RA_OK
     assert _fwd_acc(nq=0, nkv=0, q=0, k=0, v=0, out=0, lse=0, causal=0) == B.RA_OK
