@@ -576,7 +576,7 @@ def main():
                     help="minimum length of the timed oracle run for cpu_baseline")
     ap.add_argument("--lib", default=None, metavar="NAME_OR_PATH",
                     help="time another build of the library with the same C ABI: a design-choice ablation "
-                         "name (xcd_scatter, no_swizzle, no_skip, one_head, built by the build script) or a path")
+                         "name (xcd_scatter, no_swizzle, no_skip, one_head, stage_barrier, built by the build script) or a path")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (to scale the "
                          "FETCH_SIZE/WRITE_SIZE counters against a kernel of known traffic)")
