@@ -275,3 +275,35 @@ def test_reference_raise_paths(pattern, dtype):
             err = np.abs(out - ref).max()
             assert np.all(np.isfinite(out)) and err <= tol, (err, tol)
             assert np.abs(lse - ref_lse).max() <= 1e-3
+
+
+def test_concurrent_streams_give_the_same_result():
+    """The library keeps no device state between or across calls: launches of different
+    problems on two streams at once (default priority) give bit-identical results to the
+    same launches one after the other."""
+    import torch
+    import blockwise_ring_attention_amd as ra
+    say("two streams at once")
+    cases = [(1, 8, 2, 128, 512, 4, 1, True, True), (2, 4, 4, 64, 264, 3, 0, False, False)]
+    inputs = []
+    for i, (B, hq, hkv, d, n, c, rank, causal, zigzag) in enumerate(cases):
+        q, k, v = _case(B, hq, hkv, d, n, n, c, "bf16", seed=5100 + 17 * i)
+        inputs.append((to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), c, rank, causal, zigzag))
+    alone = []
+    for qd, kd, vd, c, rank, causal, zigzag in inputs:
+        out, lse = ra.rank_forward(qd, kd, vd, c, rank, causal, zigzag)
+        torch.cuda.synchronize()
+        alone.append((out.clone(), lse.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    together = []
+    for rep in range(3):
+        res = []
+        for s, (qd, kd, vd, c, rank, causal, zigzag) in zip(streams, inputs):
+            with torch.cuda.stream(s):
+                res.append(ra.rank_forward(qd, kd, vd, c, rank, causal, zigzag))
+        torch.cuda.synchronize()
+        together.append(res)
+    for res in together:
+        for (out, lse), (out0, lse0) in zip(res, alone):
+            assert torch.equal(out, out0) and torch.equal(lse, lse0)
