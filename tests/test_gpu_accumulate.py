@@ -153,3 +153,46 @@ def test_streamed_ring_full_size_32k(out32):
     ref, ref_lse = oracle.rank_forward(q, k, v, w.c, w.rank, w.causal, w.zigzag, rows=rows)
     assert_parity(o[rows[:, 0], rows[:, 1], rows[:, 2]], ref, l[rows[:, 0], rows[:, 1], rows[:, 2]], ref_lse, "bf16",
                   "accumulate 32k sampled rows")
+
+
+def test_streamed_ring_replays_in_a_graph():
+    """The streamed ring captured in a HIP graph (torch.cuda.CUDAGraph): a fill of the
+    running lse with -inf and one ra_rank_forward_accumulate launch per round. The library
+    allocates nothing and synchronizes nothing, so the captured sequence replays; every
+    replay, with unrelated eager work between replays, equals the eager run bit for bit."""
+    import torch
+    import blockwise_ring_attention_amd as ra
+    B, hq, hkv, d, n, c, rank = 1, 8, 2, 128, 512, 4, 1
+    say("streamed ring in a graph")
+    q, k, v, _ = _inputs(B, hq, hkv, d, n, c, "bf16", False, 77)
+    qd, kd, vd, _ = _device(q, k, v, None, "bf16")
+    eager_out, eager_lse = _fresh_accumulator(qd, out_f32=True)
+    for t in range(c):
+        ra.rank_forward_accumulate(qd, kd, vd, eager_out, eager_lse, c, rank, True, True, t, t + 1)
+    torch.cuda.synchronize()
+    out = torch.empty(qd.shape, dtype=torch.float32, device=qd.device)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=qd.device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm up on a side stream before capture
+        lse.fill_(float("-inf"))
+        for t in range(c):
+            ra.rank_forward_accumulate(qd, kd, vd, out, lse, c, rank, True, True, t, t + 1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lse.fill_(float("-inf"))
+        for t in range(c):
+            ra.rank_forward_accumulate(qd, kd, vd, out, lse, c, rank, True, True, t, t + 1)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out) and torch.equal(lse, eager_lse), f"replay {rep}"
+        other, _ = ra.rank_forward(qd, kd, vd, c, rank, True, True)   # eager work between replays
+        torch.cuda.synchronize()
+    ref, ref_lse = oracle.rank_forward(q, k, v, c, rank, True, True)
+    o, l = _host(out, lse)
+    assert_parity(o, ref, l, ref_lse, "bf16", "graph replay")
