@@ -292,11 +292,16 @@ def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumul
     epilogue (ra_rank_forward_accumulate, starting from lse = -inf) and rounds it to the
     input dtype once at the end; "accumulate_bf16" keeps the running out in bf16 (round 0
     a plain launch); "merge" runs plain launches and merges each later round's partial in
-    place with ra_merge. One step = all c rounds (with the fill and the final rounding).
-    Returns step ms, per-round kernel ms, per-merge ms (from one event-instrumented step),
-    and the max abs difference of the streamed result from the fused launch."""
+    place with ra_merge; "accumulate_graph" is "accumulate" captured once in a HIP graph
+    and replayed, as a rank that issues the same c launches every step would run it.
+    One step = all c rounds (with the fill and the final rounding). Returns step ms,
+    per-round kernel ms, per-merge ms (from one event-instrumented step; none for the
+    graph) and the max abs difference of the streamed result from the fused launch."""
     import torch
     import blockwise_ring_attention_amd as ra
+    graph_mode = mode == "accumulate_graph"
+    if graph_mode:
+        mode = "accumulate"
     qd, kd, vd = _device_inputs(w, arrays)
     fwd = _forward_fn(w)
     accf = _accumulate_fn(w)
@@ -335,14 +340,31 @@ def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumul
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if graph_mode:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        run = graph.replay
+        run()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
-        step()
+        run()
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / steps
+    if graph_mode:
+        round_ms, merge_ms = [], []
+        return _streamed_result(fwd, qd, kd, vd, acc, acc_lse, ms_step, round_ms, merge_ms)
     # one instrumented step: an event pair around every launch and every merge
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(c)]
     if mode == "accumulate":
@@ -360,12 +382,18 @@ def time_per_round(w, steps: int, warmup: int, arrays=None, mode: str = "accumul
     torch.cuda.synchronize()
     round_ms = [ev[t][0].elapsed_time(ev[t][1]) for t in range(c)]
     merge_ms = [ev[t][2].elapsed_time(ev[t][3]) for t in range(1, c)] if has_merge else []
+    return _streamed_result(fwd, qd, kd, vd, acc, acc_lse, ms_step, round_ms, merge_ms)
+
+
+def _streamed_result(fwd, qd, kd, vd, acc, acc_lse, ms_step, round_ms, merge_ms):
+    """The streamed result against one fused launch: max abs differences of out and lse."""
+    import torch
     fused, fused_lse = fwd(qd, kd, vd, with_lse=True)
     torch.cuda.synchronize()
     diff = (acc.float() - fused.float()).abs().max().item()
     fin = torch.isfinite(fused_lse)
     lse_diff = (acc_lse[fin] - fused_lse[fin]).abs().max().item() if bool(fin.any()) else 0.0
-    del qd, kd, vd, acc, acc32, acc_lse, part, part_lse, fused, fused_lse
+    del fused, fused_lse
     torch.cuda.empty_cache()
     return ms_step, round_ms, merge_ms, diff, lse_diff
 
@@ -683,9 +711,11 @@ def main():
                               "bf16 once at the end",
                 "accumulate_bf16": "as accumulate with the running out kept in bf16 (round 0 a plain launch)",
                 "merge": "one ra_rank_forward launch per ring round + in-place ra_merge into the running "
-                         "(out, lse)"}
+                         "(out, lse)",
+                "accumulate_graph": "accumulate captured once in a HIP graph (the lse fill, the c launches and "
+                                    "the final rounding) and replayed every step"}
         line["per_round"] = {}
-        for mode in ("accumulate", "accumulate_bf16", "merge"):
+        for mode in ("accumulate", "accumulate_bf16", "merge", "accumulate_graph"):
             ms_pr, round_ms, merge_ms, diff, lse_diff = time_per_round(w, max(1, args.steps // 4), 1, arrays, mode)
             line["per_round"][mode] = {
                 "what": what[mode],
