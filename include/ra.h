@@ -23,7 +23,11 @@
  *     return means nothing was enqueued and no output was touched; ra_last_error()
  *     then describes the problem. Inputs are not checked for NaN or infinity; results
  *     for non-finite inputs are unspecified.
- *   - Calls are reentrant; the last-error text is per host thread.
+ *   - Calls are reentrant; the last-error text is per host thread. Nothing is
+ *     synchronized or allocated, so calls on different streams may run at once and a
+ *     sequence of calls may be captured in a HIP graph and replayed.
+ *   - Output buffers must not overlap any input buffer (RA_ERR_ARG), except where an
+ *     entry point says otherwise (ra_merge's in-place update).
  */
 #ifndef RA_H
 #define RA_H
@@ -39,7 +43,8 @@ enum ra_dtype { RA_BF16 = 0, RA_F32 = 1 };
 enum ra_status {
   RA_OK = 0,
   RA_ERR_ARG = -1,         /* null pointer, c < 1, rank outside [0, c), hq % hkv != 0,
-                              negative size, bad round range, unknown dtype */
+                              negative size, bad round range, unknown dtype, outputs
+                              overlapping inputs */
   RA_ERR_SHAPE = -2,       /* causal with nq != nkv; causal zigzag with odd nkv;
                               c * nkv above 2^30 tokens, a KV head slab (nkv rows of
                               head_dim elements) above 2^31-1 bytes, or more than
