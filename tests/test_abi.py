@@ -266,3 +266,10 @@ def test_ablation_libraries_export_the_boundary():
         lib = ctypes.CDLL(path)
         for sym in _declared_functions():
             assert hasattr(lib, sym), (name, sym)
+
+
+def test_plain_c_consumer_builds(tmp_path, ra_lib):
+    """The boundary is usable from plain C: a C11 program including only ra.h and the HIP
+    runtime API compiles with gcc and links against libra.so (it runs in the GPU tests)."""
+    from tests.c_consumer import build
+    assert os.path.exists(build(str(tmp_path / "ra_c_consumer")))
