@@ -307,3 +307,35 @@ def test_concurrent_streams_give_the_same_result():
     for res in together:
         for (out, lse), (out0, lse0) in zip(res, alone):
             assert torch.equal(out, out0) and torch.equal(lse, lse0)
+
+
+@pytest.mark.parametrize("c,rank,n,causal,zigzag,doc", [
+    (32, 0, 64, True, True, False), (32, 31, 66, True, True, False), (64, 17, 32, True, False, False),
+    (64, 40, 130, True, True, True), (48, 5, 40, False, False, False),
+])
+def test_long_rings(c, rank, n, causal, zigzag, doc):
+    """Rings of 32 to 64 ranks with short blocks: the cursor walks many rounds and
+    segments per tile (most empty under the causal and document masks), fused and folded
+    round by round into an fp32 running output."""
+    import torch
+    import blockwise_ring_attention_amd as ra
+    from blockwise_ring_attention_amd.inputs import doc_start_from_lengths, draw_document_lengths
+    say(f"long ring c={c} rank={rank} n={n} causal={causal} zigzag={zigzag} doc={doc}")
+    q, k, v = _case(1, 8, 2, 128, n, n, c, "bf16", seed=6100 + c + rank)
+    ds = doc_start_from_lengths(draw_document_lengths(c * n, 300, 1.0, c + rank)) if doc else None
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    dd = torch.from_numpy(np.ascontiguousarray(ds, dtype=np.int32)).cuda() if doc else None
+    if doc:
+        out, lse = ra.rank_forward_doc(qd, kd, vd, dd, c, rank, zigzag)
+    else:
+        out, lse = ra.rank_forward(qd, kd, vd, c, rank, causal, zigzag)
+    acc = torch.empty(qd.shape, dtype=torch.float32, device=qd.device)
+    acc_lse = torch.full(qd.shape[:3], float("-inf"), device=qd.device)
+    for t in range(c):
+        ra.rank_forward_accumulate(qd, kd, vd, acc, acc_lse, c, rank, causal, zigzag, t, t + 1, doc_start=dd)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.rank_forward(q, k, v, c, rank, causal, zigzag, doc_start=ds)
+    assert_parity(out.float().cpu().numpy().astype(np.float64), ref, lse.cpu().numpy().astype(np.float64), ref_lse,
+                  "bf16", "fused")
+    assert_parity(acc.cpu().numpy().astype(np.float64), ref, acc_lse.cpu().numpy().astype(np.float64), ref_lse,
+                  "bf16", "streamed")
