@@ -160,14 +160,28 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def library_sha() -> str:
+    """sha256[:16] of the built library the bench loads (the compiled kernels themselves:
+    a source edit that leaves the shipped build unchanged, such as a diagnostic-only
+    switch, leaves it unchanged too)."""
+    from blockwise_ring_attention_amd import _binding
+    h = hashlib.sha256()
+    with open(_binding.LIB_PATH, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload: str, launch_ms: float):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on the library the bench loads; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sha") != kernel_sha():
+    try:
+        if rec.get("library_sha") != library_sha():
+            return None
+    except OSError:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -511,6 +525,110 @@ def sustain_run(w, seconds: float, flop: float, buckets: int = 12):
     return res
 
 
+def summarize_timeline(rec, kernel_ms: float):
+    """One recorded launch of the timeline build: rec is [workgroups, 8] int64 (entry,
+    after the first stage's barrier, end of the stage loop, end: ticks of the constant
+    100 MHz clock; HW_ID; XCC_ID; stages of the loop; tile)."""
+    n = int(np.count_nonzero(rec[:, 0]))
+    rec = rec[:n]
+    t = (rec[:, :4] - rec[:, 0].min()).astype(np.float64) / 100.0   # microseconds
+    folded = rec[:, 1] != 0   # tiles that folded a stage
+    hw = rec[:, 4]
+    xcc = rec[:, 5] & 0xF
+    cu = xcc * 4096 + (hw >> 8 & 0xFF)   # XCC, SE, SH and CU fields of HW_ID
+    stages = rec[:, 6].astype(np.float64)
+    prologue = (t[:, 1] - t[:, 0])[folded]
+    tail = (t[:, 3] - t[:, 2])[folded]
+    gaps, cu_end = [], {}
+    for c in np.unique(cu):
+        idx = np.where(cu == c)[0]
+        idx = idx[np.argsort(t[idx, 0])]
+        gaps.extend(t[idx[1:], 0] - t[idx[:-1], 3])
+        cu_end[int(c)] = t[idx, 3].max()
+    gaps = np.array(gaps) if gaps else np.zeros(1)
+    xcds = []
+    for x in range(8):
+        m = xcc == x
+        ends = [e for c, e in cu_end.items() if c // 4096 == x]
+        long_ = m & folded & (stages >= 8)
+        xcds.append({"xcd": x, "workgroups": int(m.sum()), "cus": len(ends),
+                     "end_us": round(float(max(ends)), 1) if ends else None,
+                     "cu_end_spread_us": round(float(max(ends) - min(ends)), 1) if ends else None,
+                     "us_per_stage": round(float((t[long_, 2] - t[long_, 1]).sum() / stages[long_].sum()), 4)
+                     if long_.any() else None})
+    ends = np.array([x["end_us"] for x in xcds if x["end_us"] is not None])
+    span = float(t[:, 3].max())
+    return {"kernel_ms": round(kernel_ms, 4), "span_us": round(span, 1), "workgroups": n,
+            "cus": len(cu_end), "xcc_is_workgroup_mod_8": bool(np.array_equal(xcc, np.arange(n) % 8)),
+            "xcd": xcds,
+            "xcd_end_mean_us": round(float(ends.mean()), 1),
+            "slowest_xcd_over_mean": round(float(ends.max() / ends.mean() - 1), 4),
+            "slowest_xcd_over_fastest": round(float(ends.max() / ends.min() - 1), 4),
+            "prologue_us_median": round(float(np.median(prologue)), 2),
+            "tail_us_median": round(float(np.median(tail)), 2),
+            "relaunch_gap_us_median": round(float(np.median(gaps)), 2),
+            "relaunch_gap_us_p90": round(float(np.percentile(gaps, 90)), 2),
+            "tiles_per_cu": round(n / max(1, len(cu_end)), 2)}
+
+
+def timeline_run(w, launches: int, warmup_ms: float = WARMUP_MS):
+    """The workload through the diagnostic build that records, per workgroup of the bf16
+    kernel, the constant 100 MHz clock at entry, after the first stage's barrier, at the
+    end of the stage loop and after the epilogue's stores, with HW_ID and XCC_ID. Warm
+    launches come first (nothing recorded), then `launches` bursts of back-to-back
+    launches, each at least 200 ms long, into the recording buffer: every launch of a
+    burst overwrites it, so it holds the burst's last launch, taken under steady load (a
+    launch that follows an idle gap runs while the clock is still settling). The output
+    must equal the shipped library's bit for bit."""
+    import ctypes
+    import torch
+    from blockwise_ring_attention_amd import _binding
+    from blockwise_ring_attention_amd.csrc import build
+    if w.dtype != "bf16":
+        raise SystemExit("--timeline records the bf16 kernel")
+    qd, kd, vd = _device_inputs(w, None)
+    fwd = _forward_fn(w)
+    out_ref = torch.empty_like(qd)
+    lse_ref = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
+    fwd(qd, kd, vd, out=out_ref, lse=lse_ref)   # the shipped library
+    torch.cuda.synchronize()
+    path = build.ablation_path("timeline")
+    lib = _binding.use_library(path)
+    lib.ra_diag_timeline.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.ra_diag_timeline.restype = ctypes.c_int
+    out = torch.empty_like(qd)
+    lse = torch.empty_like(lse_ref)
+    t_w = time.perf_counter()
+    warm = 0
+    while warm < 3 or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
+        fwd(qd, kd, vd, out=out, lse=lse)
+        warm += 1
+        torch.cuda.synchronize()
+    per_launch_ms = (time.perf_counter() - t_w) * 1e3 / warm
+    burst = max(2, int(np.ceil(200.0 / max(per_launch_ms, 1e-3))))
+    cap = 1 << 16
+    buf = torch.zeros((cap, 8), dtype=torch.int64, device="cuda")
+    rows = []
+    for _ in range(launches):
+        buf.zero_()
+        torch.cuda.synchronize()
+        assert lib.ra_diag_timeline(ctypes.c_void_p(buf.data_ptr()), cap) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(burst):
+            if i == burst - 1:
+                e0.record()
+            fwd(qd, kd, vd, out=out, lse=lse)
+        e1.record()
+        torch.cuda.synchronize()
+        assert lib.ra_diag_timeline(None, 0) == 0
+        rows.append({"burst": burst, **summarize_timeline(buf.cpu().numpy(), e0.elapsed_time(e1))})
+    identical = bool(torch.equal(out, out_ref) and torch.equal(lse, lse_ref))
+    del qd, kd, vd, out, lse, out_ref, lse_ref, buf
+    torch.cuda.empty_cache()
+    return {"library": os.path.relpath(path, ROOT), "warm_launches": warm, "identical_to_shipped": identical,
+            "launches": rows}
+
+
 def cpu_sample(w, count: int):
     """`count` query rows of batch 0 spread evenly over the share (head-major order), so
     light and heavy rows of a causal share enter in proportion, and the unmasked FLOP of
@@ -600,6 +718,10 @@ def main():
     ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
                     help="only run the workload back to back for SECONDS from idle and print the throughput "
                          "and the sampled clock and power over time")
+    ap.add_argument("--timeline", type=int, default=0, metavar="LAUNCHES",
+                    help="only run the workload through the diagnostic timeline build (built by the build "
+                         "script) and print, for each of LAUNCHES recorded launches after the warmup, the "
+                         "per-XCD finish times and stage times, and the per-tile prologue, tail and relaunch gap")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum length of the timed oracle run for cpu_baseline")
     ap.add_argument("--lib", default=None, metavar="NAME_OR_PATH",
@@ -642,6 +764,9 @@ def main():
         print(json.dumps({"balance_sweep": w.name, "c": w.c, "seq": w.seq, "steps": args.steps,
                           "warmup": args.warmup, **sweep}), flush=True)
         return
+    if args.timeline:
+        print(json.dumps({"timeline": w.name, **timeline_run(w, args.timeline, args.warmup_ms)}), flush=True)
+        return
     flop, nbytes = workload_numbers(w)
     if args.sustain:
         print(json.dumps({"sustain": w.name, **sustain_run(w, args.sustain, flop)}), flush=True)
@@ -677,6 +802,7 @@ def main():
                      "algorithmic_bytes": nbytes, "kernel_ms_avg": round(ms_launch, 4),
                      "kernel_ms_min": round(ms_min, 4), "kernel_ms_median": round(ms_med, 4)},
     }
+    line["kernel_sha"], line["library_sha"] = kernel_sha(), library_sha()
     if lib_used:
         line["library"] = os.path.relpath(lib_used, ROOT)
         line["roofline"]["traffic"] = None   # the committed counters describe the shipped kernel

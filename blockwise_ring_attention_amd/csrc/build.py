@@ -4,7 +4,8 @@ Usage: python -m blockwise_ring_attention_amd.csrc.build  [--jobs N] [--ablation
 Always recompiles; the library lands next to the package's __init__.py. With
 --ablations (or build_ablations()) it also builds one comparison library per
 design-choice switch of ra_fwd.hip / ra_host.cpp into the package's ablation/ folder:
-the same entry points and results, computed without that choice, for measurement only.
+the same entry points and results, computed without that choice, for measurement only;
+and the diagnostic build (per-workgroup timeline of the bf16 kernel) beside them.
 """
 
 from __future__ import annotations
@@ -28,6 +29,10 @@ ABLATIONS = {
     "no_skip": "RA_ABLATION_NO_SKIP",
     "one_head": "RA_ABLATION_ONE_HEAD",
     "stage_barrier": "RA_ABLATION_STAGE_BARRIER",
+}
+# Diagnostic builds, made beside the ablations: the same results, plus recording.
+DIAGNOSTICS = {
+    "timeline": "RA_DIAG_TIMELINE",   # per-workgroup clock stamps, HW_ID and XCC_ID (ra_diag_timeline)
 }
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU forms are kept out of every kernel. Inputs are taken to be NaN-free,
@@ -71,7 +76,8 @@ def ablation_path(name: str) -> str:
 
 
 def build_ablations(jobs: int = 3, verbose: bool = False) -> list[str]:
-    """One library per design-choice switch (same C ABI), for A/B measurement."""
+    """One library per design-choice switch (same C ABI), for A/B measurement, and one
+    per diagnostic switch."""
     os.makedirs(ABLATION_DIR, exist_ok=True)
     out = []
 
@@ -84,7 +90,7 @@ def build_ablations(jobs: int = 3, verbose: bool = False) -> list[str]:
         return ablation_path(name)
 
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        out = list(ex.map(one, ABLATIONS.items()))
+        out = list(ex.map(one, [*ABLATIONS.items(), *DIAGNOSTICS.items()]))
     if verbose:
         for p in out:
             print(f"built {p}")

@@ -29,6 +29,14 @@
 //   RA_ABLATION_ONE_HEAD     one query head per workgroup (no GQA head packing; ra_host.cpp);
 //   RA_ABLATION_STAGE_BARRIER a workgroup barrier before every stage instead of every pair
 //                            of stages.
+// Diagnostic build (also made by the build script, never shipped):
+//   RA_DIAG_TIMELINE         every workgroup of the bf16 kernel writes 8 words to a buffer
+//                            registered with ra_diag_timeline (below): the constant 100 MHz
+//                            clock at entry, after the first stage's barrier, at the end of
+//                            the stage loop and after the epilogue's stores, then HW_ID,
+//                            XCC_ID, the stages of the loop and the tile (row0 << 16 | KV
+//                            head). Nothing else changes, so its results are the shipped
+//                            kernel's.
 
 namespace ra {
 namespace {
@@ -57,6 +65,18 @@ constexpr float kRef0 = -1.0e30f;
 // Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: 32-bit data format,
 // no swizzle; accesses at or past num_records bytes are out of range.
 constexpr int kBufferFlags = 0x00020000;
+
+#if defined(RA_DIAG_TIMELINE)
+__device__ unsigned long long* g_timeline = nullptr;
+__device__ int g_timeline_cap = 0;
+__device__ __forceinline__ void timeline(int word, unsigned long long v) {
+  unsigned long long* t = g_timeline;
+  if (t != nullptr && threadIdx.x == 0 && (int)blockIdx.x < g_timeline_cap) t[(size_t)blockIdx.x * 8 + word] = v;
+}
+#define RA_TIMELINE(word, v) timeline(word, v)
+#else
+#define RA_TIMELINE(word, v) ((void)0)
+#endif
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -606,6 +626,10 @@ __device__ __forceinline__ void pipe_step(const FwdArgs& a, const SubInfo& si, i
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
+#if defined(RA_DIAG_TIMELINE)
+  const unsigned long long t_entry = __builtin_amdgcn_s_memrealtime();
+  int loop_stages = 0;
+#endif
   using L = Bf16Layout<D>;
   constexpr int BN = L::BN, NKS = L::NKS, NDV = L::NDV, NB = L::NB;
   static_assert(NB == 4, "stage buffers");
@@ -773,6 +797,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     // ---- stage 0 (buffer 0): steps -1 and 0
     wait_stages<D, 0>();
     phase_barrier();
+    RA_TIMELINE(1, __builtin_amdgcn_s_memrealtime());
     SubInfo prev = sub_info(cc, 1);
     {
       typename StageLoader<D>::Plan pl;
@@ -838,6 +863,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
           }
           prev = sub_info(cc, 1);
           cc.next(a, qr);
+#if defined(RA_DIAG_TIMELINE)
+          ++loop_stages;
+#endif
           if (!cc.valid) {
             last = b;
             goto tail;
@@ -846,6 +874,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
       }
     }
   tail:
+    RA_TIMELINE(2, __builtin_amdgcn_s_memrealtime());
     read_old();
     // ---- after the last stage (buffer `last`): steps 2n-1 and 2n. After an even stage
     // its V tile is complete and its first fragments were read ahead; after an odd one
@@ -876,6 +905,13 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // accumulate mode its rows whose running lse is finite stay exactly as they are, so
   // they are neither read nor written.
   const float lt = xhalf_sum(lsum);
+#if defined(RA_DIAG_TIMELINE)
+  RA_TIMELINE(0, t_entry);
+  RA_TIMELINE(4, (unsigned)__builtin_amdgcn_s_getreg((31 << 11) | 4));    // HW_ID
+  RA_TIMELINE(5, (unsigned)__builtin_amdgcn_s_getreg((31 << 11) | 20));   // XCC_ID
+  RA_TIMELINE(6, (unsigned)loop_stages);
+  RA_TIMELINE(7, ((unsigned long long)tile.row0 << 16) | (unsigned)tile.g);
+#endif
   if (!rvalid) return;
   if (a.acc && !cc_any) {
     lse_old = a.lse[ridx];
@@ -914,6 +950,12 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
       }
   }
   if (a.lse != nullptr && hf == 0) a.lse[ridx] = f.lse;
+#if defined(RA_DIAG_TIMELINE)
+  // thread 0 holds row row0 of the tile, which is never past its end, so it gets here
+  // (in plain launches) once its stores are done
+  __builtin_amdgcn_s_waitcnt(0);
+  RA_TIMELINE(3, __builtin_amdgcn_s_memrealtime());
+#endif
 }
 
 // ---------------------------------------------------------------- fp32 kernel
@@ -1062,3 +1104,19 @@ hipError_t launch_forward_f32(const FwdArgs& a, int grid, hipStream_t stream) {
 }
 
 }  // namespace ra
+
+#if defined(RA_DIAG_TIMELINE)
+// Register the timeline buffer of the diagnostic build: `capacity` workgroups of 8
+// 64-bit words (workgroups past it record nothing); nullptr and 0 unregister it. Not
+// part of the shipped library's C ABI; the caller synchronises the device around it.
+extern "C" int ra_diag_timeline(void* buf, int capacity) {
+  if (capacity < 0 || (buf == nullptr) != (capacity == 0)) return -1;
+  const int zero = 0;
+  unsigned long long* p = static_cast<unsigned long long*>(buf);
+  if (hipMemcpyToSymbol(HIP_SYMBOL(ra::g_timeline_cap), &zero, sizeof(int)) != hipSuccess ||
+      hipMemcpyToSymbol(HIP_SYMBOL(ra::g_timeline), &p, sizeof(p)) != hipSuccess ||
+      hipMemcpyToSymbol(HIP_SYMBOL(ra::g_timeline_cap), &capacity, sizeof(int)) != hipSuccess)
+    return -5;
+  return 0;
+}
+#endif

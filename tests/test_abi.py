@@ -259,13 +259,29 @@ def test_ablation_libraries_export_the_boundary():
     and export every entry point the header declares, so the bench can time them through
     the same calls."""
     from blockwise_ring_attention_amd.csrc import build
-    for name in build.ABLATIONS:
+    for name in [*build.ABLATIONS, *build.DIAGNOSTICS]:
         path = build.ablation_path(name)
         if not os.path.exists(path):
             pytest.skip(f"{path} not built (build_ablations)")
         lib = ctypes.CDLL(path)
         for sym in _declared_functions():
             assert hasattr(lib, sym), (name, sym)
+
+
+def test_timeline_registration_only_in_the_diagnostic_build(ra_lib):
+    """ra_diag_timeline exists only in the diagnostic build, and rejects a buffer without
+    a capacity (and the reverse) before touching the device."""
+    from blockwise_ring_attention_amd.csrc import build
+    assert not hasattr(ra_lib, "ra_diag_timeline")
+    path = build.ablation_path("timeline")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not built (build_ablations)")
+    lib = ctypes.CDLL(path)
+    lib.ra_diag_timeline.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.ra_diag_timeline.restype = ctypes.c_int
+    assert lib.ra_diag_timeline(None, 4) == -1
+    assert lib.ra_diag_timeline(ctypes.c_void_p(4096), 0) == -1
+    assert lib.ra_diag_timeline(ctypes.c_void_p(4096), -1) == -1
 
 
 def test_plain_c_consumer_builds(tmp_path, ra_lib):

@@ -175,16 +175,17 @@ def test_bench_break_even_context():
     assert ctx["min_chunk_tokens_to_hide_on_one_link"] == pytest.approx(1250e12 * w.hkv / (153e9 * w.hq), rel=1e-4)
 
 
-def test_bench_traffic_only_for_the_profiled_kernel(monkeypatch):
-    """roofline.traffic comes from the committed counter profile only while the kernel
-    sources still hash to the sha the profile was taken on; otherwise it is null."""
+def test_bench_traffic_only_for_the_profiled_kernel(monkeypatch, ra_lib):
+    """roofline.traffic comes from the committed counter profile only while the library
+    the bench loads is the build the profile was taken on; otherwise it is null."""
     import bench
     rec = json.load(open(os.path.join(os.path.dirname(bench.__file__), "profiles",
                                       "traffic_gqa64x8_d128_s128k_c16_zigzag_bf16.json")))
+    assert len(rec["library_sha"]) == 16 and len(rec["kernel_sha"]) == 16
     got = bench.measured_traffic("gqa64x8_d128_s128k_c16_zigzag_bf16", 14.0)
-    if rec["kernel_sha"] == bench.kernel_sha():
+    if rec["library_sha"] == bench.library_sha():
         assert got == pytest.approx(rec["hbm_bytes_per_launch"])
     else:
         assert got is None
-    monkeypatch.setattr(bench, "kernel_sha", lambda: "0" * 16)
+    monkeypatch.setattr(bench, "library_sha", lambda: "0" * 16)
     assert bench.measured_traffic("gqa64x8_d128_s128k_c16_zigzag_bf16", 14.0) is None
