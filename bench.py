@@ -32,7 +32,7 @@ PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 matrix
 METRIC = "attention TFLOP/s (unmasked) per rank share, 1 GPU; % of bf16 MFMA peak"
 DEFAULT_WORKLOAD = "gqa64x8_d128_s128k_c16_zigzag_bf16"
 ALSO_WORKLOADS = ["gqa32x8_d128_s32k_c8_zigzag_bf16", "mha16_b2_d128_s64k_c8_noncausal_outliers_bf16",
-                  "mha_d64_s4k_c4_zigzag_fp32"]
+                  "mha_d64_s4k_c4_zigzag_fp32", "gqa32x8_d128_s32k_c8_zigzag_fp32"]
 MIN_TIMED_MS = 200.0   # short workloads get more steps so the timed region spans this much
 WARMUP_MS = 1000.0     # warmup runs at least this long: the chip's clock ramps up under load
 KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_ring_attention_amd", "csrc", f)
@@ -559,7 +559,10 @@ def summarize_timeline(rec, kernel_ms: float):
     ends = np.array([x["end_us"] for x in xcds if x["end_us"] is not None])
     span = float(t[:, 3].max())
     return {"kernel_ms": round(kernel_ms, 4), "span_us": round(span, 1), "workgroups": n,
-            "cus": len(cu_end), "xcc_is_workgroup_mod_8": bool(np.array_equal(xcc, np.arange(n) % 8)),
+            "cus": len(cu_end),
+            # workgroup i ran on XCD (i + o) mod 8 for one o (the round-robin's starting
+            # XCD, where the previous dispatch left off), else None
+            "xcd_offset": int(xcc[0]) if np.array_equal(xcc, (np.arange(n) + xcc[0]) % 8) else None,
             "xcd": xcds,
             "xcd_end_mean_us": round(float(ends.mean()), 1),
             "slowest_xcd_over_mean": round(float(ends.max() / ends.mean() - 1), 4),

@@ -961,14 +961,19 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
 // ---------------------------------------------------------------- fp32 kernel
 // Same fold with v_mfma_f32_32x32x2f32 (fp32 in, fp32 accumulate), one column block per
 // wave, K/V tiles of 32 rows in LDS. DP = head_dim rounded up to 32; dims beyond
-// head_dim are zero-filled and skipped.
+// head_dim are zero in Q and in the LDS tiles, so their products add exact zeros and
+// need no test. The next tile's rows are loaded into registers (16-byte loads) while the
+// current one is folded, and written to LDS once every wave is done with it.
 template <int DP>
 __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   constexpr int BN = 32;
   constexpr int KSF = DP + 2;   // K row stride (floats): 64 distinct banks per read
   constexpr int VSF = DP + 8;   // V row stride (floats): the two halves hit disjoint banks
-  __shared__ float kl[BN * KSF];
-  __shared__ float vl[BN * VSF];
+  constexpr int C4 = DP / 4;    // 16-byte chunks of a padded row
+  constexpr int PER = BN * C4 / 256;   // chunks of K (and of V) per thread per tile
+  static_assert(PER * 256 == BN * C4, "whole chunks per thread");
+  __shared__ __attribute__((aligned(16))) float kl[BN * KSF];
+  __shared__ __attribute__((aligned(16))) float vl[BN * VSF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, col = lane & 31;
@@ -1002,24 +1007,54 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   const size_t blk_stride = (size_t)a.B * a.hkv * a.nkv * d;
   const size_t head_off = ((size_t)tile.b * a.hkv + tile.g) * a.nkv * d;
 
+  // Thread tid stages chunks tid + 256 j of a tile: row idx / C4, columns 4 (idx % C4)
+  // .. +3 (zeros past head_dim; head_dim is a multiple of 8, so no chunk straddles it).
+  // Rows past the block's end repeat its last row; the mask drops them.
+  f32x4 kr[PER], vr[PER];
+  auto load_tile = [&](const KvCursor<BN>& c) {
+    const float* kb = kg + c.blk * blk_stride + head_off;
+    const float* vb = vg + c.blk * blk_stride + head_off;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int idx = tid + 256 * j;
+      const int cx = 4 * (idx % C4);
+      const size_t src = (size_t)min(c.r + idx / C4, a.nkv - 1) * d + cx;
+      const bool in = cx < d;
+      kr[j] = in ? *reinterpret_cast<const f32x4*>(kb + src) : f32x4{0.f, 0.f, 0.f, 0.f};
+      vr[j] = in ? *reinterpret_cast<const f32x4*>(vb + src) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int idx = tid + 256 * j;
+      const int rr = idx / C4, cx = 4 * (idx % C4);
+      // K rows start 8-byte aligned (the stride is DP + 2): two 8-byte writes
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      f32x2* kd = reinterpret_cast<f32x2*>(kl + rr * KSF + cx);
+      kd[0] = f32x2{kr[j][0], kr[j][1]};
+      kd[1] = f32x2{kr[j][2], kr[j][3]};
+      *reinterpret_cast<f32x4*>(vl + rr * VSF + cx) = vr[j];
+    }
+  };
+
+  // The cursor's validity is the same in every wave (it follows the tile's query range).
   KvCursor<BN> cur;
   cur.begin(a, qr);
+  if (cur.valid) {
+    load_tile(cur);
+    store_tile();
+  }
   while (cur.valid) {
-    __syncthreads();
-    const float* kb = kg + cur.blk * blk_stride + head_off;
-    const float* vb = vg + cur.blk * blk_stride + head_off;
-    for (int idx = tid; idx < BN * DP; idx += 256) {
-      const int rr = idx / DP, cx = idx % DP;
-      const size_t src = (size_t)min(cur.r + rr, a.nkv - 1) * d + cx;
-      kl[rr * KSF + cx] = cx < d ? kb[src] : 0.f;
-      vl[rr * VSF + cx] = cx < d ? vb[src] : 0.f;
-    }
-    __syncthreads();
+    __syncthreads();   // the tile of `cur` is in LDS
+    KvCursor<BN> nxt = cur;
+    nxt.next(a, qr);
+    if (nxt.valid) load_tile(nxt);   // in flight while this tile is folded
 
     f32x16 s = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < DP / 2; ++ks)
-      if (2 * ks < d) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kl[col * KSF + 2 * ks + hf], qf[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(kl[col * KSF + 2 * ks + hf], qf[ks], s, 0, 0, 0);
     if (cur.r > cur.mrow || cur.r < cur.mlow) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -1048,13 +1083,13 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int dv = 0; dv < DP / 32; ++dv)
-      if (32 * dv < d) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          o[dv] = __builtin_amdgcn_mfma_f32_32x32x2f32(vl[(8 * (e >> 2) + 4 * hf + (e & 3)) * VSF + 32 * dv + col],
-                                                       s[e], o[dv], 0, 0, 0);
-      }
-    cur.next(a, qr);
+      for (int e = 0; e < 16; ++e)
+        o[dv] = __builtin_amdgcn_mfma_f32_32x32x2f32(vl[(8 * (e >> 2) + 4 * hf + (e & 3)) * VSF + 32 * dv + col],
+                                                     s[e], o[dv], 0, 0, 0);
+    __syncthreads();   // every wave is done reading this tile
+    if (nxt.valid) store_tile();
+    cur = nxt;
   }
 
   const float lt = xhalf_sum(lsum);

@@ -49,7 +49,10 @@ class Workload:
         return self.seq // self.c
 
 
-# The five workloads the method is measured and checked on.
+# The workloads the method is measured and checked on: the two fp32 parity shapes, the
+# 32k and 128k GQA shares, the 64k non-causal share with key outliers, the 128k share
+# with packed documents, and the 32k share's shape in fp32 (the fp32 path at a size that
+# fills the GPU).
 WORKLOADS = {
     w.name: w
     for w in [
@@ -67,6 +70,8 @@ WORKLOADS = {
         Workload("gqa64x8_d128_s128k_c16_zigzag_docs_bf16", "bf16", 1, 64, 8, 128, 131072, 16, 0, True, True, 0.5, 3,
                  doc_median=8192, doc_sigma=1.0,
                  notes="the 128k share with a packed-document mask: lognormal document lengths, median 8192"),
+        Workload("gqa32x8_d128_s32k_c8_zigzag_fp32", "f32", 1, 32, 8, 128, 32768, 8, 3, True, True, 0.5, 5,
+                 notes="the 32k share's shape in fp32"),
     ]
 }
 

@@ -75,7 +75,11 @@ def test_timeline_records_without_changing_the_result():
     assert folded.any()
     assert (r[folded, 0] <= r[folded, 1]).all() and (r[folded, 1] <= r[folded, 2]).all()
     assert (r[folded, 2] <= r[folded, 3]).all() and (r[:, 0] <= r[:, 3]).all()
-    assert np.array_equal(r[:, 5] & 0xF, np.arange(n_wg) % 8), "workgroup i runs on XCD i mod 8"
+    # workgroups are dealt round-robin to the 8 XCDs, starting where the previous dispatch
+    # left off: workgroup i runs on XCD (i + o) mod 8 with one o per launch, so workgroups
+    # i and i + 8 share an XCD (what the kernel's KV-head pinning relies on)
+    off = ((r[:, 5] & 0xF) - np.arange(n_wg)) % 8
+    assert (off == off[0]).all(), "workgroups i and i + 8 share an XCD"
     assert (r[:, 6] >= 0).all() and (r[:, 7] & 0xFFFF < hkv).all()
     assert ((r[:, 7] >> 16) < n).all()
 
