@@ -189,3 +189,43 @@ def test_bench_traffic_only_for_the_profiled_kernel(monkeypatch, ra_lib):
         assert got is None
     monkeypatch.setattr(bench, "library_sha", lambda: "0" * 16)
     assert bench.measured_traffic("gqa64x8_d128_s128k_c16_zigzag_bf16", 14.0) is None
+
+
+def test_bench_timeline_summary_of_a_known_recording():
+    """bench.summarize_timeline on a hand-built recording (2 XCDs' worth of CUs, ticks of
+    the 100 MHz clock): XCD ends, per-XCD stage time, prologue, tail, relaunch gap and
+    the round-robin offset come out as constructed."""
+    import bench
+    rows = []
+    # 16 workgroups, starting XCD 3: workgroup i on XCD (i + 3) % 8; two per XCD, both
+    # on one CU of that XCD, back to back. Each: entry, +400 ticks (4 us) to the first
+    # barrier, 10 stages of 170 ticks, +500 ticks (5 us) of tail, then a 250-tick gap.
+    t_next = {}
+    for i in range(16):
+        x = (i + 3) % 8
+        cu_field = 5   # same CU index on every XCD
+        start = t_next.get(x, 1000 + 50 * x)
+        slow = 1.0 + 0.01 * x   # XCD x runs (1 + x/100) slower
+        t1 = start + 400
+        t2 = t1 + int(round(10 * 170 * slow))
+        t3 = t2 + 500
+        t_next[x] = t3 + 250
+        rows.append([start, t1, t2, t3, cu_field << 8, x, 10, (32 * i) << 16 | (i % 4)])
+    rec = np.zeros((64, 8), dtype=np.int64)
+    rec[:16] = np.array(rows, dtype=np.int64)
+    s = bench.summarize_timeline(rec, kernel_ms=0.05)
+    assert s["workgroups"] == 16 and s["cus"] == 8 and s["tiles_per_cu"] == 2.0
+    assert s["xcd_offset"] == 3
+    assert s["prologue_us_median"] == pytest.approx(4.0) and s["tail_us_median"] == pytest.approx(5.0)
+    assert s["relaunch_gap_us_median"] == pytest.approx(2.5)
+    t0 = min(r[0] for r in rows)
+    for x in s["xcd"]:
+        mine = [r for r in rows if r[5] == x["xcd"]]
+        assert x["workgroups"] == 2 and x["cus"] == 1
+        assert x["end_us"] == pytest.approx((max(r[3] for r in mine) - t0) / 100.0, abs=0.05)
+        assert x["us_per_stage"] == pytest.approx(1.7 * (1.0 + 0.01 * x["xcd"]), rel=2e-3)
+    ends = np.array([x["end_us"] for x in s["xcd"]])
+    assert s["slowest_xcd_over_mean"] == pytest.approx(ends.max() / ends.mean() - 1, abs=1e-4)
+    # a recording whose XCDs do not follow one round-robin offset reports none
+    rec[1, 5] = 7
+    assert bench.summarize_timeline(rec, kernel_ms=0.05)["xcd_offset"] is None
