@@ -15,7 +15,7 @@ from tests.gpu_util import assert_parity, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 128
+N_CASES = 512
 
 
 def _draw(i):
