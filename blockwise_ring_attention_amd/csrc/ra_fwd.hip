@@ -783,40 +783,39 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     // in flight into the other buffers. Even sub-tiles use (sA, pA), odd ones (sB, pB).
     // Every pair issues its loads, empty ones past the end of the stream (into buffers
     // nothing reads again), so the loads need no branch and can sit inside the steps.
+    // The first pair (stages 0, 1) has no previous pair: the tile's start issues, besides
+    // its own K0, V0 and K1, the next pair's K2, K3, V1 and V2 into the still unused
+    // buffers, and waits only for the first three before stage 0 (stage 0 reads K0, and at
+    // its end K1 and V0): the later four, issued last, stay in flight behind the first.
     typename StageLoader<D>::Plan pend;
     {
       const typename StageLoader<D>::Plan p0 = plan_next();
       ld.issue_k(p0, kb[0]);
       ld.issue_v(p0, vb[0]);
+      const typename StageLoader<D>::Plan p1 = plan_next();
+      ld.issue_k(p1, kb[1]);
+      ld.issue_v(p1, vb[1]);
+      const typename StageLoader<D>::Plan p2 = plan_next();
+      ld.issue_k(p2, kb[2]);
+      ld.issue_v(p2, vb[2]);
       pend = plan_next();
-      ld.issue_k(pend, kb[1]);
+      ld.issue_k(pend, kb[3]);
     }
     f32x16 sA, sB;
     bf16x8 pA[2], pB[2];
     Frags<D> fr;   // LDS fragments in flight, read ahead across steps (see pipe_block)
-    // ---- stage 0 (buffer 0): steps -1 and 0
-    wait_stages<D, 0>();
+    // ---- stage 0 (buffer 0): steps -1 and 0; the last two stages' loads may be in flight
+    wait_stages<D, 2>();
     phase_barrier();
     RA_TIMELINE(1, __builtin_amdgcn_s_memrealtime());
     SubInfo prev = sub_info(cc, 1);
     {
-      typename StageLoader<D>::Plan pl;
       pipe_step<D, true, false, false>(a, prev, hf, qds, qpos, sc, kb[0], vb[0], qf, koff, voff, pB, o, sA, sB, pB,
-                                       mref, lsum, fr, nullptr, nullptr, [&] {
-                                         ld.issue_v(pend, vb[1]);
-                                         pl = plan_at(lc);
-                                         ld.issue_k(pl, kb[2]);
-                                       });
-      if (lc.valid) lc.next(a, qr);
+                                       mref, lsum, fr);
       // ... reads the first K fragments of stage 1 and V^T fragments of stage 0 for step 1
       pipe_step<D, true, false, true, false, false, true, true>(a, sub_info(cc, 0), hf, qds, qpos, sc,
                                                                 kb[0] + 32 * L::ROWB, vb[0], qf, koff, voff, pB, o,
-                                                                sB, sA, pA, mref, lsum, fr, kb[1], vb[0], [&] {
-                                                                  ld.issue_v(pl, vb[2]);
-                                                                  pend = plan_at(lc);
-                                                                  ld.issue_k(pend, kb[3]);
-                                                                });
-      if (lc.valid) lc.next(a, qr);
+                                                                sB, sA, pA, mref, lsum, fr, kb[1], vb[0]);
     }
     cc.next(a, qr);
     int last = 0;   // buffer of the last stage, for the tail
