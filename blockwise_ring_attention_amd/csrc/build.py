@@ -44,7 +44,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "inclu
 
 def _compile(src: str, build_dir: str, defines=()) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(HERE, src), "-o", obj]
+    # A fixed compilation-unit ID per source: hipcc otherwise derives it from the source's
+    # path and writes it into symbol names, so the same sources built in another
+    # directory would give a library with other bytes.
+    cuid = "ra_" + os.path.splitext(src)[0]
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, f"-cuid={cuid}", *[f"-D{d}" for d in defines], "-c",
+           os.path.join(HERE, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
